@@ -1,0 +1,140 @@
+"""Pins of the oracle's statistics and quantize steps: inputs built so the
+right answer is known by construction, error bounds of round-to-nearest, and
+cross-checks against library routines."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import E2M1, E4M3, decode
+from workloads import WORKLOADS, draw, to_bf16_bits
+
+
+def _bits(x):
+    return to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_channel_mean_by_construction():
+    """K = c_d + a zero-mean +-r pattern: the mean is c_d exactly."""
+    B, H, N, D = 1, 2, 96, 128
+    c = (np.arange(D, dtype=np.float32) / 8 - 5)[None, None, None, :]
+    r = np.where(np.arange(N) % 2 == 0, 1.5, -1.5).astype(np.float32)[None, None, :, None]
+    k = oracle.bf16_bits_to_f64(_bits(c + r * np.ones((B, H, N, D), np.float32)))
+    mu, vmax = oracle.channel_stats(k, -2.0 * k)
+    assert np.array_equal(mu, np.broadcast_to(c[:, :, 0, :], mu.shape))
+    assert np.array_equal(vmax, np.abs(2.0 * k).max(axis=2).astype(np.float32))
+
+
+def test_channel_mean_agrees_with_numpy_mean():
+    w = WORKLOADS["tiny"]
+    _, kb, vb = draw(w)
+    k = oracle.bf16_bits_to_f64(kb)
+    mu, _ = oracle.channel_stats(k, k)
+    ref = k.mean(axis=2).astype(np.float32)
+    ulp = np.spacing(np.abs(ref))
+    assert np.all(np.abs(mu - ref) <= ulp)
+
+
+def test_fp8_block_scales_by_construction():
+    """Block t holds max |x| = 2^t at one element: scale 2^t/448, code +-448."""
+    B, H, N, D, blk = 1, 1, 100, 128, 32         # 4 blocks, the last one short (4 tokens)
+    rng = np.random.default_rng(3)
+    x = (rng.uniform(-0.9, 0.9, (B, H, N, D))).astype(np.float32)
+    for t in range(4):
+        n0 = t * blk
+        x[0, 0, n0:n0 + blk] *= np.float32(2.0 ** t)
+        x[0, 0, n0 + 1, 7 + t] = np.float32((-1) ** t * 2.0 ** t)
+    codes, scales = oracle.quantize_fp8_blocks(x, blk)
+    assert scales.shape == (1, 1, 4)
+    for t in range(4):
+        assert scales[0, 0, t] == np.float32(np.float32(2.0 ** t) / np.float32(448))
+        assert codes[0, 0, t * blk + 1, 7 + t] == (0x7E if t % 2 == 0 else 0xFE)
+    vals = decode(codes, E4M3) * np.repeat(scales[0, 0].astype(np.float64), blk)[None, None, :N, None]
+    err = np.abs(vals - x)
+    s_tok = np.repeat(scales[0, 0].astype(np.float64), blk)[:N][None, None, :, None]
+    normal = np.abs(x) >= s_tok * 2.0 ** -6
+    assert np.all(err[normal] <= (2.0 ** -4 + 1e-6) * np.abs(x[normal]))
+    assert np.all(err[~normal] <= (2.0 ** -10 + 1e-7) * np.broadcast_to(s_tok, x.shape)[~normal])
+
+
+def test_zero_block_gives_zero_scale_and_codes():
+    x = np.zeros((1, 1, 130, 128), np.float32)
+    x[0, 0, 64:] = 1.0
+    codes, scales = oracle.quantize_fp8_blocks(x, 64)
+    assert scales[0, 0, 0] == 0 and np.all(codes[0, 0, :64] == 0)
+    assert scales[0, 0, 1] == np.float32(1.0 / 448) and np.all(codes[0, 0, 64:] == 0x7E)
+
+
+def test_fp4_groups_and_nibble_order():
+    """One token whose first group spans the full E2M1 range (scale 1), so
+    the codes are read off the format table; the even channel is the low nibble."""
+    x = np.zeros((1, 1, 1, 128), np.float32)
+    x[0, 0, 0, :8] = [6.0, -6.0, 3.0, 0.5, 1.5, -4.0, 0.75, 2.5]
+    x[0, 0, 0, 16:32] = 12.0                     # second group: scale 2, all codes 6.0 -> 0x7
+    packed, scales = oracle.quantize_fp4_groups(x)
+    assert packed.shape == (1, 1, 1, 64) and scales.shape == (1, 1, 1, 8)
+    assert scales[0, 0, 0, 0] == 1.0 and scales[0, 0, 0, 1] == 2.0 and scales[0, 0, 0, 2] == 0.0
+    # codes: 6->7, -6->F, 3->5, 0.5->1, 1.5->3, -4->E, 0.75->2 (ties to 1.0), 2.5->4 (ties to 2.0)
+    assert list(packed[0, 0, 0, :4]) == [0xF7, 0x15, 0xE3, 0x42]
+    assert np.all(packed[0, 0, 0, 8:16] == 0x77)
+    assert np.all(packed[0, 0, 0, 16:] == 0)
+    assert np.array_equal(oracle.unpack_fp4(packed)[0, 0, 0, :8], [7, 15, 5, 1, 3, 14, 2, 4])
+
+
+def test_fp4_error_bound():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((1, 2, 50, 128)).astype(np.float32)
+    packed, scales = oracle.quantize_fp4_groups(x)
+    vals = decode(oracle.unpack_fp4(packed), E2M1).reshape(1, 2, 50, 8, 16)
+    s = scales.astype(np.float64)[..., None]
+    xg = x.reshape(1, 2, 50, 8, 16).astype(np.float64)
+    err = np.abs(vals * s - xg)
+    y = np.abs(xg) / s
+    bound = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0)) * s + 1e-6 * np.abs(xg)
+    assert np.all(err <= bound)
+    assert np.all(np.abs(vals).max(axis=-1) == 6.0)
+
+
+def test_v_channel_max_maps_to_448():
+    w = WORKLOADS["tiny"]
+    _, _, vb = draw(w)
+    v = oracle.bf16_bits_to_f64(vb)
+    vmax = np.abs(v).max(axis=2).astype(np.float32)
+    codes, scales = oracle.quantize_v(v, vmax)
+    vals = decode(codes, E4M3)
+    assert np.all(np.abs(vals).max(axis=2) == 448.0)
+    assert np.all(scales == (vmax / np.float32(448)).astype(np.float32))
+
+
+def test_k_smoothing_removes_constant_key_offset_exactly():
+    """Adding a constant vector to every key moves the mean by exactly that
+    vector (values chosen so every step is exact), so the K codes and scales
+    are bit-identical."""
+    rng = np.random.default_rng(5)
+    B, H, N, D = 1, 1, 256, 128
+    k = (np.round(rng.uniform(-7, 7, (B, H, N, D)) * 16) / 16).astype(np.float32)
+    c = rng.integers(-8, 9, D).astype(np.float32)
+    q = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    z1 = oracle.quantize(_bits(q), _bits(k), _bits(v), block_q=64, block_k=64)
+    z2 = oracle.quantize(_bits(q), _bits(k + c), _bits(v), block_q=64, block_k=64)
+    assert np.array_equal(z2.k_mean, z1.k_mean + c)
+    assert np.array_equal(z1.k_codes, z2.k_codes) and np.array_equal(z1.k_scales, z2.k_scales)
+    for fmt in ("fp4",):
+        a = oracle.quantize(_bits(q), _bits(k), _bits(v), fmt=fmt)
+        b = oracle.quantize(_bits(q), _bits(k + c), _bits(v), fmt=fmt)
+        assert np.array_equal(a.k_codes, b.k_codes) and np.array_equal(a.k_scales, b.k_scales)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dev1024"])
+def test_fp64_key_sum_is_exact_in_any_order(name):
+    """For the synthetic inputs every partial sum of K over tokens is exactly
+    representable in fp64 (all values are multiples of 2^q and the sum of
+    magnitudes is below 2^(q+53)), so any summation order gives the exact sum."""
+    w = WORKLOADS[name]
+    _, kb, _ = draw(w, heads=min(w.heads, 4))
+    k = oracle.bf16_bits_to_f64(kb)
+    nz = k[k != 0]
+    _, e = np.frexp(np.abs(nz))
+    q = (e - 1).min() - 7                       # smallest ulp among the bf16 values
+    top = np.log2(np.abs(k).sum(axis=2).max())
+    assert top - q < 53

@@ -1,0 +1,99 @@
+"""Seeded synthetic inputs for the quantized attention path.
+
+This module only draws inputs: it holds none of the method's arithmetic, and
+both the HIP path's tests/benchmark and the CPU oracle take their inputs from
+it.  The pages measure on FLUX image generation and Kontext edits (prompts,
+calibration pairs and example images none of which are available); these
+draws stand in for them with the token counts of those workloads:
+
+* image tokens = (resolution / 16)**2 (8x VAE downsampling, then 2x2 patches),
+  plus 512 text tokens;
+* Kontext edits append 4096 context-image tokens after the 4096 output-image
+  tokens (NVIDIA RTX AI, 저정밀 양자화로 FLUX.1 Kontext 최적화, hyper.ai/kr: the
+  input image becomes tokens concatenated with the output-image tokens);
+* the 2048x2048 case batches a classifier-free-guidance pair (B = 2), the
+  grouping the VisualGen article uses across GPUs (FLUX 3 Image Klein Base,
+  devotd.net, "왜 이런 차이가 나나").
+
+Draw recipe (per workload, seed = 1000 + workload id): NumPy PCG64 streams
+spawned from ``SeedSequence(seed)`` in the order Q, K-noise, V, K-offset,
+ctx-Q, ctx-K, ctx-V; every draw is ``standard_normal(float32)``.  Q, V ~ N(0,1);
+K = noise + offset with a per-channel offset of standard deviation 3, shape
+[1, H, 1, D], broadcast over batch and tokens (K's channel outliers).  In the
+Kontext workload the context tokens are 0.8 * (matching output-image token)
++ 0.6 * fresh noise, for Q, K-noise and V (correlation 0.8, unit variance).
+Inputs are rounded to bfloat16, nearest-even.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+HEAD_DIM = 128
+TAU = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
+
+
+@dataclass(frozen=True)
+class Workload:
+    wid: int
+    name: str
+    batch: int
+    heads: int
+    seq_len: int
+    fmt: str          # "fp8" or "fp4" (Q/K precision; P and V are FP8 in both)
+    block_q: int
+    block_k: int
+    text_tokens: int
+    image_tokens: int
+    context_tokens: int = 0
+
+    @property
+    def flops(self) -> float:
+        """Dense attention FLOPs 4 B H N^2 D (two contractions)."""
+        return 4.0 * self.batch * self.heads * self.seq_len ** 2 * HEAD_DIM
+
+
+WORKLOADS = {
+    "tiny": Workload(1, "tiny", 1, 2, 320, "fp8", 64, 64, 64, 256),
+    "schnell512": Workload(2, "schnell512", 4, 24, 1536, "fp8", 128, 64, 512, 1024),
+    "dev1024": Workload(3, "dev1024", 1, 24, 4608, "fp8", 128, 64, 512, 4096),
+    "kontext1024": Workload(4, "kontext1024", 1, 24, 8704, "fp8", 128, 64, 512, 4096, 4096),
+    "gen2048_fp8": Workload(5, "gen2048_fp8", 2, 24, 16896, "fp8", 128, 64, 512, 16384),
+    "gen2048_fp4": Workload(5, "gen2048_fp4", 2, 24, 16896, "fp4", 128, 64, 512, 16384),
+}
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, nearest-even (inputs only)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def draw(w: Workload, batch: int | None = None, heads: int | None = None, seq_len: int | None = None,
+         seed: int | None = None):
+    """Q, K, V bf16 bit patterns (uint16 [B, H, N, 128]) for workload ``w``.
+
+    ``batch``/``heads``/``seq_len``/``seed`` override the workload's sizes for
+    edge cases; the Kontext correlation applies only at its full length."""
+    B = w.batch if batch is None else batch
+    H = w.heads if heads is None else heads
+    N = w.seq_len if seq_len is None else seq_len
+    D = HEAD_DIM
+    ss = np.random.SeedSequence(1000 + w.wid if seed is None else seed)
+    rq, rk, rv, ro, cq, ck, cv = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(7))
+    q = rq.standard_normal((B, H, N, D), dtype=np.float32)
+    kn = rk.standard_normal((B, H, N, D), dtype=np.float32)
+    v = rv.standard_normal((B, H, N, D), dtype=np.float32)
+    offset = (np.float32(3.0) * ro.standard_normal((1, H, 1, D), dtype=np.float32)).astype(np.float32)
+    if w.context_tokens and N == w.seq_len:
+        out0 = w.text_tokens
+        c0 = w.text_tokens + w.image_tokens
+        nc = w.context_tokens
+        for arr, r in ((q, cq), (kn, ck), (v, cv)):
+            z = r.standard_normal((B, H, nc, D), dtype=np.float32)
+            arr[:, :, c0:c0 + nc] = (np.float32(0.8) * arr[:, :, out0:out0 + nc] + np.float32(0.6) * z)
+    k = (kn + offset).astype(np.float32)
+    return to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v)
