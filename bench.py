@@ -1,0 +1,167 @@
+"""Throughput of quantized SDPA (FP8 Q/K/P/V) on one MI355X.
+
+One step = one qsdpa_forward call over the Kontext-style 1024x1024 edit
+sequence (512 text + 4096 output-image + 4096 context-image tokens, B=1,
+H=24, head_dim 128): channel statistics, quantize, fused attention, bf16 out.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line: TFLOP/s of the whole step (4 B H N^2 D per step), the
+roofline of the dominant kernel (the fused attention, timed with HIP events
+on the stream it runs on) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="kontext1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="query rows of the CPU oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_attn_fp8_kontext1024.json"),
+                    help="HBM bytes per attention launch measured with rocprofv3 counters (if present)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, rows: int):
+    """The oracle, single process with single-threaded BLAS, on one (b, h)
+    and ``rows`` query rows against all keys (quantize of that head included)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import TAU, draw
+
+    qb, kb, vb = draw(w, batch=1)
+    qb, kb, vb = qb[:1, :1], kb[:1, :1], vb[:1, :1]
+    rows_idx = np.arange(rows)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        z = oracle.quantize(qb, kb, vb, fmt=w.fmt, block_q=w.block_q, block_k=w.block_k)
+        oracle.attend(z, TAU, 0, 0, rows_idx)
+        dt = time.perf_counter() - t0
+    flops = 4.0 * rows * w.seq_len * 128
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"(b,h)=(0,0) of {w.name}: quantize of the head + {rows} query rows x {w.seq_len} keys "
+                      f"({dt:.2f} s wall, single-threaded NumPy)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by (batch, head) with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import precision_attention_qsdpa_amd as qs
+    from workloads import TAU, WORKLOADS, draw
+
+    w = WORKLOADS[args.workload]
+    qb, kb, vb = draw(w)
+    dev = torch.device("cuda:0")
+    to = lambda x: torch.from_numpy(x).view(torch.bfloat16).to(dev)
+    q, k, v = to(qb), to(kb), to(vb)
+    params = qs.make_params(w.batch, w.heads, w.seq_len, fmt=w.fmt, block_q=w.block_q, block_k=w.block_k,
+                            softmax_scale=TAU)
+    ws = qs.empty_workspace(params, dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        qs.qsdpa_forward(q, k, v, out=out, workspace=ws, params=params, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # dominant kernel (fused attention) and the quantize pass, timed alone
+    n_attn = max(args.steps, 20)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(n_attn):
+        qs.qsdpa_attention(ws, out, params, stream=stream)
+    a1.record(stream)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(n_attn):
+        qs.qsdpa_quantize(q, k, v, ws, params, stream=stream)
+    b1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_attn = a0.elapsed_time(a1) / n_attn
+    ms_quant = b0.elapsed_time(b1) / n_attn
+
+    flops = w.flops
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("workload") == w.name and tj.get("kernel_source_sha") == kernel_sha():
+            traffic = tj.get("hbm_bytes_per_launch")
+    elem = w.batch * w.heads * w.seq_len * 128
+    rec = {
+        "metric": "quantized SDPA TFLOPS at FLUX shapes (N=4608/8704/16896) + % FP8 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if w.fmt == "fp8" else "fp4_e2m1+fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) Q/V, K with N(0,3) channel offsets; Kontext context tokens rho=0.8)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "head_dim": 128, "qk_format": w.fmt, "block_q": w.block_q, "block_k": w.block_k,
+                   "pct_fp8_peak": round(100.0 * tflops / FP8_PEAK_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel<fp8>", "achieved": round(attn_tflops, 2),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
+        "quantize": {"ms_per_launch": round(ms_quant, 4),
+                     "algorithmic_GB_s": round(elem * 13 / (ms_quant * 1e-3) / 1e9, 1),
+                     "hbm_peak_GB_s": HBM_PEAK_GBS},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+def kernel_sha() -> str:
+    """Hash of the attention kernel source (the traffic counters are only
+    valid for the kernel they were taken on)."""
+    import hashlib
+    p = os.path.join(ROOT, "precision_attention_qsdpa_amd", "csrc", "qsdpa_attn.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

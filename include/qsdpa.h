@@ -1,0 +1,149 @@
+/*
+ * qsdpa.h - C ABI of quantized scaled-dot-product attention for MI355X (gfx950).
+ *
+ * The operation.  Attention softmax(tau * Q K^T) V over one joint token
+ * sequence per (batch, head) - text tokens, then image tokens, then (for
+ * Kontext edits) context-image tokens, with no mask - computed with FP8 or
+ * FP4 operands.  The pages describe quantizing the SDPA of the FLUX
+ * transformer as the core of the work, with FP8 and FP4 schemes that differ
+ * only in the precision of the query/key side while attention itself stays
+ * FP8 (NVIDIA RTX AI optimiert FLUX.1 fuer Bilddaten mit niedriger
+ * Genauigkeit, hyper.ai/de; NVIDIA RTX AI, 저정밀 양자화로 FLUX.1 Kontext 최적화,
+ * hyper.ai/kr); Kontext concatenates the input-image tokens to the output-image
+ * tokens (same articles).  They print no formula; the steps below are the
+ * reading this library implements:
+ *
+ *   1. per (b,h,d): mu = fp32(sum_n K / N) (sum in fp64), vmax = max_n |V|;
+ *   2. Ks = fp32(K - mu) (K smoothing: softmax is unchanged by it);
+ *   3. FP8 mode: Q per block of block_q tokens, Ks per block of block_k
+ *      tokens, scale s = fp32(amax/448), code = E4M3(fp32(x * fp32(448/amax)));
+ *      FP4 mode: per token and 16 consecutive channels, s = fp32(amax/6),
+ *      code = E2M1(fp32(x * fp32(6/amax))); an all-zero block has s = 0 and
+ *      zero codes.  E4M3/E2M1 round to nearest even and saturate;
+ *   4. V per channel: sV = fp32(vmax/448), code = E4M3(fp32(V * fp32(448/vmax)));
+ *   5. scores S = tau * dequant(Q) . dequant(K);
+ *   6. online softmax over steps of 64 keys in ascending order:
+ *      m = running max, p = exp(S - m), P = E4M3(448 p) fed to an FP8 P.V
+ *      product, l = sum of the unquantized p, accumulators rescaled by
+ *      exp(m_old - m_new);
+ *   7. O = bf16_rne(acc * sV / (448 l)).
+ *
+ * Conventions for every entry point:
+ *   - Q, K, V, O are device pointers to contiguous bf16 [B, H, N, 128]
+ *     tensors owned by the caller; the workspace is a caller-owned device
+ *     buffer of at least qsdpa_workspace_bytes() bytes.
+ *   - Device pointers must be 16-byte aligned, the workspace 256-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; the library never allocates, frees or
+ *     synchronizes, and keeps no state between calls (thread-safe).
+ *   - Every argument is validated before the first launch: a negative status
+ *     means nothing was enqueued (except QSDPA_ERR_HIP, which reports a failed
+ *     launch).  Nothing throws across the ABI.  Inputs must be finite.
+ */
+#ifndef QSDPA_H
+#define QSDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSDPA_ABI_VERSION 1
+#define QSDPA_HEAD_DIM 128
+
+/* Status codes (return values). */
+#define QSDPA_OK 0
+#define QSDPA_ERR_INVALID_ARG (-1)         /* null pointer, size <= 0 or overflowing, bad scale */
+#define QSDPA_ERR_UNSUPPORTED (-2)         /* head_dim != 128, block sizes, format, group size */
+#define QSDPA_ERR_ALIGNMENT (-3)           /* a pointer is not 16 B (workspace: 256 B) aligned */
+#define QSDPA_ERR_WORKSPACE_TOO_SMALL (-4) /* ws_bytes < qsdpa_workspace_bytes() */
+#define QSDPA_ERR_ALIAS (-5)               /* O overlaps an input or the workspace */
+#define QSDPA_ERR_HIP (-6)                 /* a kernel launch failed */
+
+/* Q/K precision.  P and V are FP8 E4M3 in both. */
+#define QSDPA_QK_FP8_E4M3 0
+#define QSDPA_QK_FP4_E2M1 1
+
+typedef struct qsdpa_params {
+  int32_t batch;         /* B >= 1 */
+  int32_t heads;         /* H >= 1 */
+  int32_t seq_len;       /* N >= 1 (any value: tails are handled) */
+  int32_t head_dim;      /* must be 128 */
+  int32_t block_q;       /* FP8 mode: Q tokens per scale, 64 or 128 (ignored in FP4 mode) */
+  int32_t block_k;       /* FP8 mode: K tokens per scale, must be 64 (ignored in FP4 mode) */
+  int32_t qk_format;     /* QSDPA_QK_FP8_E4M3 or QSDPA_QK_FP4_E2M1 */
+  int32_t fp4_group;     /* FP4 mode: channels per scale, must be 16 (ignored in FP8 mode) */
+  float softmax_scale;   /* tau > 0 and finite, normally 1/sqrt(128) */
+} qsdpa_params;
+
+/*
+ * Byte offsets of the workspace sections (filled by qsdpa_workspace_layout).
+ * N is padded to n_pad = round_up(N, 128); padded tokens hold zero codes.
+ * BH = B*H, (b,h) index bh = b*H + h.
+ *   q_codes, k_codes: uint8 [BH][n_pad][code_row_bytes]; FP8: one E4M3 code
+ *                     per channel; FP4: two E2M1 codes per byte, the even
+ *                     channel in the low nibble.
+ *   q_scales:         fp32 [BH][q_scale_count]; FP8: per block_q tokens
+ *                     (q_scale_count = n_pad/block_q, blocks past N are 0);
+ *                     FP4: [BH][n_pad][8], one per 16 channels.
+ *   k_scales:         as q_scales with block_k.
+ *   k_mean:           fp32 [BH][128] (mu).
+ *   v_codes:          uint8 [BH][n_pad/64][128][64]: for each 64-key tile,
+ *                     channel-major rows of 64 codes in a fixed key order:
+ *                     byte p of a row holds key 32*kb + 8*(r>>2) + 4*g + (r&3)
+ *                     with g = p>>5, kb = (p>>4)&1, r = p&15.
+ *   v_scales:         fp32 [BH][128] (sV).
+ *   v_amax:           fp32 [BH][128] (vmax).
+ *   stats:            scratch for partial channel sums (fp64) and maxima.
+ */
+typedef struct qsdpa_layout {
+  uint64_t q_codes, q_scales, k_codes, k_scales, k_mean, v_codes, v_scales, v_amax, stats;
+  uint64_t total;          /* bytes needed (= qsdpa_workspace_bytes) */
+  int32_t n_pad;
+  int32_t code_row_bytes;  /* 128 (FP8) or 64 (FP4) */
+  int32_t q_scale_count;   /* per (b,h) */
+  int32_t k_scale_count;   /* per (b,h) */
+  int32_t stats_splits;    /* token ranges of the statistics pass */
+  int32_t reserved[3];
+} qsdpa_layout;
+
+/* ABI version (QSDPA_ABI_VERSION of the built library). */
+int qsdpa_abi_version(void);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* qsdpa_status_string(int status);
+
+/* Validate parameters (host only, no GPU call).  Returns a status. */
+int qsdpa_validate_params(const qsdpa_params* p);
+
+/* Workspace bytes for p, or 0 if p is invalid.  No GPU call. */
+size_t qsdpa_workspace_bytes(const qsdpa_params* p);
+
+/* Fill *out with the workspace layout for p.  No GPU call.  Returns a status. */
+int qsdpa_workspace_layout(const qsdpa_params* p, qsdpa_layout* out);
+
+/*
+ * Steps 1-4: channel statistics, K smoothing and the Q/K/V codes and scales,
+ * written into the workspace (layout above).  q, k, v: bf16 [B,H,N,128].
+ */
+int qsdpa_quantize(const qsdpa_params* p, const void* q, const void* k, const void* v,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Steps 5-7 on a workspace filled by qsdpa_quantize with the same params:
+ * writes O bf16 [B,H,N,128].
+ */
+int qsdpa_attention(const qsdpa_params* p, const void* workspace, size_t ws_bytes, void* o,
+                    void* stream);
+
+/* qsdpa_quantize followed by qsdpa_attention on the same stream. */
+int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSDPA_H */

@@ -1,0 +1,179 @@
+"""Python binding of ``libqsdpa.so``: quantized scaled-dot-product attention
+for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/qsdpa.h``.  PyTorch supplies
+device memory and the stream.  There is no fallback: if the library is not
+built, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqsdpa.so")
+
+QSDPA_OK = 0
+QSDPA_ERR_INVALID_ARG = -1
+QSDPA_ERR_UNSUPPORTED = -2
+QSDPA_ERR_ALIGNMENT = -3
+QSDPA_ERR_WORKSPACE_TOO_SMALL = -4
+QSDPA_ERR_ALIAS = -5
+QSDPA_ERR_HIP = -6
+QSDPA_QK_FP8_E4M3 = 0
+QSDPA_QK_FP4_E2M1 = 1
+HEAD_DIM = 128
+
+EXPORTS = ("qsdpa_abi_version", "qsdpa_status_string", "qsdpa_validate_params", "qsdpa_workspace_bytes",
+           "qsdpa_workspace_layout", "qsdpa_quantize", "qsdpa_attention", "qsdpa_forward")
+
+
+class QsdpaParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("qk_format", ctypes.c_int32), ("fp4_group", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class QsdpaLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("q_codes", "q_scales", "k_codes", "k_scales", "k_mean",
+                                               "v_codes", "v_scales", "v_amax", "stats", "total")] + \
+               [(n, ctypes.c_int32) for n in ("n_pad", "code_row_bytes", "q_scale_count", "k_scale_count",
+                                              "stats_splits")] + [("reserved", ctypes.c_int32 * 3)]
+
+
+class QsdpaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m precision_attention_qsdpa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(QsdpaParams)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.qsdpa_abi_version.restype = ctypes.c_int
+    lib.qsdpa_abi_version.argtypes = []
+    lib.qsdpa_status_string.restype = ctypes.c_char_p
+    lib.qsdpa_status_string.argtypes = [ctypes.c_int]
+    lib.qsdpa_validate_params.restype = ctypes.c_int
+    lib.qsdpa_validate_params.argtypes = [P]
+    lib.qsdpa_workspace_bytes.restype = sz
+    lib.qsdpa_workspace_bytes.argtypes = [P]
+    lib.qsdpa_workspace_layout.restype = ctypes.c_int
+    lib.qsdpa_workspace_layout.argtypes = [P, ctypes.POINTER(QsdpaLayout)]
+    lib.qsdpa_quantize.restype = ctypes.c_int
+    lib.qsdpa_quantize.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.qsdpa_attention.restype = ctypes.c_int
+    lib.qsdpa_attention.argtypes = [P, vp, sz, vp, vp]
+    lib.qsdpa_forward.restype = ctypes.c_int
+    lib.qsdpa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().qsdpa_status_string(int(status)).decode()
+
+
+def make_params(batch: int, heads: int, seq_len: int, *, fmt: str = "fp8", block_q: int = 128,
+                block_k: int = 64, softmax_scale: float | None = None, head_dim: int = HEAD_DIM,
+                fp4_group: int = 16) -> QsdpaParams:
+    if fmt not in ("fp8", "fp4"):
+        raise ValueError(f"fmt must be 'fp8' or 'fp4', not {fmt!r}")
+    tau = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
+    return QsdpaParams(batch, heads, seq_len, head_dim, block_q, block_k,
+                       QSDPA_QK_FP8_E4M3 if fmt == "fp8" else QSDPA_QK_FP4_E2M1, fp4_group, tau)
+
+
+def qsdpa_validate_params(params: QsdpaParams) -> int:
+    return load().qsdpa_validate_params(ctypes.byref(params))
+
+
+def qsdpa_workspace_bytes(params: QsdpaParams) -> int:
+    return int(load().qsdpa_workspace_bytes(ctypes.byref(params)))
+
+
+def qsdpa_workspace_layout(params: QsdpaParams) -> QsdpaLayout:
+    out = QsdpaLayout()
+    st = load().qsdpa_workspace_layout(ctypes.byref(params), ctypes.byref(out))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_workspace_layout")
+    return out
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check_qkv(t, params: QsdpaParams, name: str):
+    import torch
+    shape = (params.batch, params.heads, params.seq_len, params.head_dim)
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+        raise ValueError(f"{name} must be a contiguous CUDA bfloat16 tensor of shape {shape}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def empty_workspace(params: QsdpaParams, device=None):
+    """A uint8 device tensor big enough for ``params`` (256-byte aligned)."""
+    import torch
+    n = qsdpa_workspace_bytes(params)
+    if n == 0:
+        raise QsdpaError(qsdpa_validate_params(params), "qsdpa_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def qsdpa_quantize(q, k, v, workspace, params: QsdpaParams, stream=None) -> None:
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_qkv(t, params, n)
+    st = load().qsdpa_quantize(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_quantize")
+
+
+def qsdpa_attention(workspace, out, params: QsdpaParams, stream=None) -> None:
+    _check_qkv(out, params, "out")
+    st = load().qsdpa_attention(ctypes.byref(params), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), out.data_ptr(), _stream(stream))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_attention")
+
+
+def qsdpa_forward(q, k, v, out=None, workspace=None, *, fmt: str = "fp8", block_q: int = 128,
+                  block_k: int = 64, softmax_scale: float | None = None, params: QsdpaParams | None = None,
+                  stream=None):
+    """O = quantized SDPA(q, k, v) for bf16 [B, H, N, 128] CUDA tensors."""
+    import torch
+    if params is None:
+        B, H, N, Dh = q.shape
+        params = make_params(B, H, N, fmt=fmt, block_q=block_q, block_k=block_k,
+                             softmax_scale=softmax_scale, head_dim=Dh)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_qkv(t, params, n)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(out, params, "out")
+    if workspace is None:
+        workspace = empty_workspace(params, q.device)
+    st = load().qsdpa_forward(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_forward")
+    return out

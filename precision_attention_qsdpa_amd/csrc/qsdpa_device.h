@@ -1,0 +1,59 @@
+// Device-side helpers of the quantized attention kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsdpa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;          // head dimension
+constexpr int KSTEP = 64;       // keys per online-softmax step (also the K scale block)
+constexpr int NPAD = 128;       // token padding of every workspace tensor
+constexpr float FP8_MAX = 448.f;
+constexpr float FP4_MAX = 6.f;
+constexpr float LOG2_448 = 8.807354922057604f;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// The two bf16 values held in one 32-bit word (low half = first element).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two fp32 -> two E4M3 codes in the low (hi_word = false) or high 16 bits of
+// `old`.  The hardware conversion rounds to nearest even, keeps the sign and
+// handles subnormals; magnitudes at or above 464 would become NaN, so callers
+// clamp values that can reach them.
+template <bool HI_WORD>
+__device__ __forceinline__ int cvt_e4m3x2(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI_WORD);
+}
+
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -FP8_MAX), FP8_MAX); }
+
+// E2M1 code of fp32 x with |x| <= 6, round to nearest even, sign kept.
+// Magnitude thresholds: ties at 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 go to
+// the neighbour with an even mantissa bit.
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  float y = fabsf(x);
+  uint32_t c = (y > 0.25f) + (y >= 0.75f) + (y > 1.25f) + (y >= 1.75f) + (y > 2.5f) +
+               (y >= 3.5f) + (y > 5.0f);
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace qsdpa

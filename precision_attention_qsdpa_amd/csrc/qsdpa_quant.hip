@@ -1,0 +1,286 @@
+// Statistics and quantize kernels: channel mean of K and max |V| (fp64 /
+// fp32), K smoothing, per-block FP8 / per-16-channel FP4 codes of Q and K,
+// per-channel FP8 codes of V written as key-tiles in the order the attention
+// kernel's value product consumes them.
+//
+// All of these kernels are bound by HBM traffic; they read bf16 rows with
+// 16-byte loads, 16 threads per 256-byte token row.
+//
+// Every fp32 operation that decides a code (K - mu, F / amax, amax / F,
+// x * inv) is a single correctly rounded IEEE operation, so the codes and
+// scales are bit-identical to a plain CPU evaluation of the same steps.
+#include "qsdpa_device.h"
+#include "qsdpa_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace qsdpa {
+
+// ---------------------------------------------------------------------------
+// Channel statistics, pass 1: per (b,h, token range of STATS_ROWS tokens)
+// partial fp64 sums of K and fp32 maxima of |V| over the range.
+// grid = (splits, BH), block = 256: thread = (row lane 0..15, 8 channels).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stats_partial_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int splits,
+    double* __restrict__ psum, float* __restrict__ pmax) {
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, cg = tid & 15, rl = tid >> 4;
+  const size_t base = (size_t)bh * N * D + cg * 8;
+  const int n0 = split * STATS_ROWS, n1 = min(N, n0 + STATS_ROWS);
+  double s[8];
+  float m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { s[j] = 0.0; m[j] = 0.f; }
+  for (int n = n0 + rl; n < n1; n += 16) {
+    const u32x4 kk = *(const u32x4*)(k + base + (size_t)n * D);
+    const u32x4 vv = *(const u32x4*)(v + base + (size_t)n * D);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[2 * j] += (double)bf16_lo(kk[j]);
+      s[2 * j + 1] += (double)bf16_hi(kk[j]);
+      m[2 * j] = fmaxf(m[2 * j], fabsf(bf16_lo(vv[j])));
+      m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(bf16_hi(vv[j])));
+    }
+  }
+  __shared__ double lsum[16][D];
+  __shared__ float lmax[16][D];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { lsum[rl][cg * 8 + j] = s[j]; lmax[rl][cg * 8 + j] = m[j]; }
+  __syncthreads();
+  if (tid < D) {
+    double t = 0.0;
+    float mm = 0.f;
+    for (int r = 0; r < 16; ++r) { t += lsum[r][tid]; mm = fmaxf(mm, lmax[r][tid]); }
+    psum[((size_t)bh * splits + split) * D + tid] = t;
+    pmax[((size_t)bh * splits + split) * D + tid] = mm;
+  }
+}
+
+// Pass 2: per (b,h), combine the ranges: mu = fp32(fp64 sum / N),
+// vmax = max, sV = fp32(vmax / 448).  grid = BH, block = 128 (one channel each).
+__global__ __launch_bounds__(128) void stats_final_kernel(
+    const double* __restrict__ psum, const float* __restrict__ pmax, int N, int splits,
+    float* __restrict__ mu, float* __restrict__ vamax, float* __restrict__ vscale) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  double t = 0.0;
+  float mm = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    t += psum[((size_t)bh * splits + s) * D + d];
+    mm = fmaxf(mm, pmax[((size_t)bh * splits + s) * D + d]);
+  }
+  mu[bh * D + d] = (float)(t / (double)N);
+  vamax[bh * D + d] = mm;
+  vscale[bh * D + d] = mm > 0.f ? mm / FP8_MAX : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 codes of one token block of Q (mu == nullptr) or of smoothed K.
+// block = 256 threads: thread = (row lane rl, channel group cg of 8); rows
+// rl, rl+16, ... of the block.  Rows at or past N get zero codes.
+// ---------------------------------------------------------------------------
+template <int BLK>
+__device__ __forceinline__ void fp8_block(const uint16_t* __restrict__ x, const float* __restrict__ mu,
+                                          uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                          int N, int n_pad, int bh, int blk, float* red) {
+  constexpr int RPT = BLK / 16;
+  const int tid = threadIdx.x, cg = tid & 15, rl = tid >> 4;
+  const int n0 = blk * BLK;
+  float val[RPT][8];
+  float mloc[8];
+  if (mu) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mloc[j] = mu[bh * D + cg * 8 + j];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int n = n0 + rl + 16 * i;
+    if (n < N) {
+      const u32x4 w = *(const u32x4*)(x + ((size_t)bh * N + n) * D + cg * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { val[i][2 * j] = bf16_lo(w[j]); val[i][2 * j + 1] = bf16_hi(w[j]); }
+      if (mu) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) val[i][j] = val[i][j] - mloc[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(val[i][j]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) val[i][j] = 0.f;
+    }
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.f ? FP8_MAX / amax : 0.f;
+  if (tid == 0) scales[blk] = amax > 0.f ? amax / FP8_MAX : 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int n = n0 + rl + 16 * i;
+    u32x2 out = {0u, 0u};
+    if (amax > 0.f && n < N) {
+      int lo = cvt_e4m3x2<false>(clamp448(val[i][0] * inv), clamp448(val[i][1] * inv), 0);
+      lo = cvt_e4m3x2<true>(clamp448(val[i][2] * inv), clamp448(val[i][3] * inv), lo);
+      int hi = cvt_e4m3x2<false>(clamp448(val[i][4] * inv), clamp448(val[i][5] * inv), 0);
+      hi = cvt_e4m3x2<true>(clamp448(val[i][6] * inv), clamp448(val[i][7] * inv), hi);
+      out[0] = (uint32_t)lo;
+      out[1] = (uint32_t)hi;
+    }
+    *(u32x2*)(codes + ((size_t)bh * n_pad + n) * D + cg * 8) = out;
+  }
+}
+
+// grid = (q_blocks + k_blocks, BH): the first q_blocks blocks quantize Q
+// (block_q tokens each), the rest quantize smoothed K (64 tokens each).
+template <int BQ>
+__global__ __launch_bounds__(256) void quant_qk_fp8_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
+    uint8_t* __restrict__ qc, float* __restrict__ qs, uint8_t* __restrict__ kc,
+    float* __restrict__ ks, int N, int n_pad) {
+  __shared__ float red[4];
+  const int bh = blockIdx.y;
+  const int qb = n_pad / BQ;
+  const int b = blockIdx.x;
+  if (b < qb) {
+    fp8_block<BQ>(q, nullptr, qc, qs + (size_t)bh * qb, N, n_pad, bh, b, red);
+  } else {
+    fp8_block<KSTEP>(k, mu, kc, ks + (size_t)bh * (n_pad / KSTEP), N, n_pad, bh, b - qb, red);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP4 codes: one thread per (token, 16-channel group).  grid = (n_pad/32, BH, 2)
+// (z = 0: Q, z = 1: smoothed K), block = 256 = 32 tokens x 8 groups.
+// Codes [BH][n_pad][64] (even channel in the low nibble), scales [BH][n_pad][8].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_qk_fp4_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
+    uint8_t* __restrict__ qc, float* __restrict__ qs, uint8_t* __restrict__ kc,
+    float* __restrict__ ks, int N, int n_pad) {
+  const int bh = blockIdx.y;
+  const bool is_k = blockIdx.z == 1;
+  const uint16_t* x = is_k ? k : q;
+  uint8_t* codes = is_k ? kc : qc;
+  float* scales = is_k ? ks : qs;
+  const int tid = threadIdx.x, grp = tid & 7;
+  const int n = blockIdx.x * 32 + (tid >> 3);
+  float val[16];
+  float amax = 0.f;
+  if (n < N) {
+    const u32x4* src = (const u32x4*)(x + ((size_t)bh * N + n) * D + grp * 16);
+    const u32x4 w0 = src[0], w1 = src[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      val[2 * j] = bf16_lo(w0[j]);
+      val[2 * j + 1] = bf16_hi(w0[j]);
+      val[8 + 2 * j] = bf16_lo(w1[j]);
+      val[8 + 2 * j + 1] = bf16_hi(w1[j]);
+    }
+    if (is_k) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) val[j] = val[j] - mu[bh * D + grp * 16 + j];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(val[j]));
+  }
+  u32x2 out = {0u, 0u};
+  float scale = 0.f;
+  if (amax > 0.f) {
+    const float inv = FP4_MAX / amax;
+    scale = amax / FP4_MAX;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float y = fminf(fmaxf(val[j] * inv, -FP4_MAX), FP4_MAX);
+      out[j >> 3] |= e2m1_code(y) << (4 * (j & 7));
+    }
+  }
+  *(u32x2*)(codes + ((size_t)bh * n_pad + n) * (D / 2) + grp * 8) = out;
+  scales[((size_t)bh * n_pad + n) * 8 + grp] = scale;
+}
+
+// ---------------------------------------------------------------------------
+// V codes, written as 64-key tiles [128 channels][64 keys] in the key order of
+// the value product's B operand: byte p of a channel row holds key
+// 32*kb + 8*(r>>2) + 4*g + (r&3) with g = p>>5, kb = (p>>4)&1, r = p&15.
+// grid = (n_pad/64, BH), block = 256.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int vtile_pos(int key) {
+  const int kb = key >> 5, w = key & 31;
+  const int r = ((w >> 3) << 2) | (w & 3);
+  const int g = (w >> 2) & 1;
+  return 32 * g + 16 * kb + r;
+}
+
+__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
+                                                      const float* __restrict__ vamax,
+                                                      uint8_t* __restrict__ vc, int N, int n_pad) {
+  __shared__ uint8_t tile[D * KSTEP];
+  const int t = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, cg = tid & 15, rl = tid >> 4;
+  float inv[8];
+  bool nz[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float a = vamax[bh * D + cg * 8 + j];
+    nz[j] = a > 0.f;
+    inv[j] = nz[j] ? FP8_MAX / a : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = rl + 16 * i;
+    const int n = t * KSTEP + key;
+    float val[8];
+    if (n < N) {
+      const u32x4 w = *(const u32x4*)(v + ((size_t)bh * N + n) * D + cg * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { val[2 * j] = bf16_lo(w[j]); val[2 * j + 1] = bf16_hi(w[j]); }
+    }
+    const int pos = vtile_pos(key);
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      int c = 0;
+      if (n < N) c = cvt_e4m3x2<false>(clamp448(val[j] * inv[j]), clamp448(val[j + 1] * inv[j + 1]), 0);
+      const uint32_t c0 = (n < N && nz[j]) ? (uint32_t)(c & 0xff) : 0u;
+      const uint32_t c1 = (n < N && nz[j + 1]) ? (uint32_t)((c >> 8) & 0xff) : 0u;
+      tile[(cg * 8 + j) * KSTEP + pos] = (uint8_t)c0;
+      tile[(cg * 8 + j + 1) * KSTEP + pos] = (uint8_t)c1;
+    }
+  }
+  __syncthreads();
+  const u32x4* src = (const u32x4*)tile;
+  u32x4* dst = (u32x4*)(vc + ((size_t)bh * (n_pad / KSTEP) + t) * (D * KSTEP));
+  dst[tid] = src[tid];
+  dst[tid + 256] = src[tid + 256];
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers.
+// ---------------------------------------------------------------------------
+void launch_quantize(const LaunchArgs& a, hipStream_t s) {
+  const int BH = a.batch * a.heads;
+  stats_partial_kernel<<<dim3(a.stats_splits, BH), 256, 0, s>>>(
+      (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_len, a.stats_splits, (double*)a.stats_sum,
+      (float*)a.stats_max);
+  stats_final_kernel<<<BH, 128, 0, s>>>((const double*)a.stats_sum, (const float*)a.stats_max,
+                                        a.seq_len, a.stats_splits, a.k_mean, a.v_amax, a.v_scales);
+  if (a.fp4) {
+    quant_qk_fp4_kernel<<<dim3(a.n_pad / 32, BH, 2), 256, 0, s>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
+        a.k_scales, a.seq_len, a.n_pad);
+  } else if (a.block_q == 128) {
+    quant_qk_fp8_kernel<128><<<dim3(a.n_pad / 128 + a.n_pad / KSTEP, BH), 256, 0, s>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
+        a.k_scales, a.seq_len, a.n_pad);
+  } else {
+    quant_qk_fp8_kernel<64><<<dim3(a.n_pad / 64 + a.n_pad / KSTEP, BH), 256, 0, s>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
+        a.k_scales, a.seq_len, a.n_pad);
+  }
+  quant_v_kernel<<<dim3(a.n_pad / KSTEP, BH), 256, 0, s>>>((const uint16_t*)a.v, a.v_amax, a.v_codes,
+                                                            a.seq_len, a.n_pad);
+}
+
+}  // namespace qsdpa

@@ -1,0 +1,78 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+library through its binding, and read the workspace back in the oracle's
+natural layouts.  (No arithmetic of the method lives here.)"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import precision_attention_qsdpa_amd as qs
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def vtile_key_order() -> np.ndarray:
+    """key held by byte p of a V tile row (documented in include/qsdpa.h)."""
+    p = np.arange(64)
+    g, kb, r = p >> 5, (p >> 4) & 1, p & 15
+    return 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3)
+
+
+def read_workspace(ws: torch.Tensor, params, N: int) -> dict:
+    """Workspace sections as numpy arrays in natural layouts, tokens < N."""
+    L = qs.qsdpa_workspace_layout(params)
+    BH = params.batch * params.heads
+    B, H = params.batch, params.heads
+    raw = ws.cpu().numpy()
+
+    def sec(off, count, dtype):
+        return raw[off:off + count * np.dtype(dtype).itemsize].view(dtype)
+
+    crb = L.code_row_bytes
+    out = {}
+    out["q_codes"] = sec(L.q_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, :N]
+    out["k_codes"] = sec(L.k_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, :N]
+    if params.qk_format == qs.QSDPA_QK_FP8_E4M3:
+        nq = -(-N // params.block_q)
+        nk = -(-N // params.block_k)
+        out["q_scales"] = sec(L.q_scales, BH * L.q_scale_count, np.float32).reshape(B, H, -1)[:, :, :nq]
+        out["k_scales"] = sec(L.k_scales, BH * L.k_scale_count, np.float32).reshape(B, H, -1)[:, :, :nk]
+        out["q_scales_pad"] = sec(L.q_scales, BH * L.q_scale_count, np.float32).reshape(B, H, -1)[:, :, nq:]
+        out["k_scales_pad"] = sec(L.k_scales, BH * L.k_scale_count, np.float32).reshape(B, H, -1)[:, :, nk:]
+    else:
+        out["q_scales"] = sec(L.q_scales, BH * L.q_scale_count, np.float32).reshape(B, H, L.n_pad, 8)[:, :, :N]
+        out["k_scales"] = sec(L.k_scales, BH * L.k_scale_count, np.float32).reshape(B, H, L.n_pad, 8)[:, :, :N]
+    out["k_mean"] = sec(L.k_mean, BH * 128, np.float32).reshape(B, H, 128)
+    out["v_scales"] = sec(L.v_scales, BH * 128, np.float32).reshape(B, H, 128)
+    out["v_amax"] = sec(L.v_amax, BH * 128, np.float32).reshape(B, H, 128)
+    vt = sec(L.v_codes, BH * L.n_pad * 128, np.uint8).reshape(B, H, L.n_pad // 64, 128, 64)
+    nat = np.empty((B, H, L.n_pad // 64, 64, 128), np.uint8)
+    nat[:, :, :, vtile_key_order(), :] = vt.transpose(0, 1, 2, 4, 3)
+    nat = nat.reshape(B, H, L.n_pad, 128)
+    out["v_codes"] = nat[:, :, :N]
+    out["v_codes_pad"] = nat[:, :, N:]
+    out["q_codes_pad"] = sec(L.q_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, N:]
+    out["k_codes_pad"] = sec(L.k_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, N:]
+    return out
+
+
+def run_quantize(q_bits, k_bits, v_bits, params):
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    ws = qs.empty_workspace(params)
+    ws.fill_(0xA5)   # poison: every byte the layout promises must be written
+    qs.qsdpa_quantize(q, k, v, ws, params)
+    torch.cuda.synchronize()
+    return ws
+
+
+def run_forward(q_bits, k_bits, v_bits, params):
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    out = qs.qsdpa_forward(q, k, v, params=params)
+    torch.cuda.synchronize()
+    return from_dev(out)

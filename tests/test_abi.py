@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU call is made): the library loads,
+exports every function that include/qsdpa.h declares, validates arguments and
+lays out the workspace as documented.  Every forward/quantize call here is
+rejected by validation before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_attention_qsdpa_amd as qs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "qsdpa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsdpa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = qs.load()
+    names = _header_functions()
+    assert set(names) == set(qs.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_abi_version_and_status_strings():
+    assert qs.load().qsdpa_abi_version() == 1
+    for st in range(-6, 1):
+        assert qs.status_string(st) not in ("", "unknown status")
+    assert qs.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(batch=0), qs.QSDPA_ERR_INVALID_ARG), (dict(heads=-1), qs.QSDPA_ERR_INVALID_ARG),
+    (dict(seq_len=0), qs.QSDPA_ERR_INVALID_ARG), (dict(head_dim=64), qs.QSDPA_ERR_UNSUPPORTED),
+    (dict(block_q=96), qs.QSDPA_ERR_UNSUPPORTED), (dict(block_k=128), qs.QSDPA_ERR_UNSUPPORTED),
+    (dict(qk_format=7), qs.QSDPA_ERR_UNSUPPORTED), (dict(softmax_scale=0.0), qs.QSDPA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("inf")), qs.QSDPA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), qs.QSDPA_ERR_INVALID_ARG),
+    (dict(batch=70000), qs.QSDPA_ERR_UNSUPPORTED),
+    (dict(batch=4096, heads=16, seq_len=1 << 22), qs.QSDPA_ERR_UNSUPPORTED),
+    (dict(batch=256, heads=128, seq_len=1 << 21), qs.QSDPA_ERR_INVALID_ARG),
+])
+def test_invalid_params(change, status):
+    p = qs.make_params(1, 2, 320)
+    for k, v in change.items():
+        setattr(p, k, v)
+    assert qs.qsdpa_validate_params(p) == status
+    assert qs.qsdpa_workspace_bytes(p) == 0
+    lib = qs.load()
+    assert lib.qsdpa_forward(ctypes.byref(p), 256, 256, 256, 1 << 40, 1 << 41, 1 << 30, None) == status
+
+
+def test_fp4_group_checked_only_in_fp4_mode():
+    p = qs.make_params(1, 1, 64, fmt="fp4", fp4_group=32)
+    assert qs.qsdpa_validate_params(p) == qs.QSDPA_ERR_UNSUPPORTED
+    p = qs.make_params(1, 1, 64, fmt="fp8", fp4_group=32)
+    assert qs.qsdpa_validate_params(p) == qs.QSDPA_OK
+    p = qs.make_params(1, 1, 64, fmt="fp4", block_q=96)      # block sizes unused in FP4 mode
+    assert qs.qsdpa_validate_params(p) == qs.QSDPA_OK
+
+
+def _round(x, a):
+    return (x + a - 1) // a * a
+
+
+@pytest.mark.parametrize("B,H,N,fmt,bq", [(1, 2, 320, "fp8", 64), (1, 24, 8704, "fp8", 128),
+                                          (2, 24, 16896, "fp4", 128), (3, 5, 1, "fp8", 128),
+                                          (1, 1, 1000, "fp4", 64)])
+def test_workspace_closed_form(B, H, N, fmt, bq):
+    """One byte per Q/K code in FP8 mode (half a byte in FP4 mode), one byte per
+    V code, fp32 scales, padded to 128 tokens, 256-byte aligned sections."""
+    p = qs.make_params(B, H, N, fmt=fmt, block_q=bq)
+    L = qs.qsdpa_workspace_layout(p)
+    BH, npad = B * H, _round(N, 128)
+    splits = -(-N // 256)
+    crb = 128 if fmt == "fp8" else 64
+    qsc = npad // bq if fmt == "fp8" else npad * 8
+    ksc = npad // 64 if fmt == "fp8" else npad * 8
+    sizes = [BH * npad * crb, BH * npad * crb, BH * npad * 128, BH * qsc * 4, BH * ksc * 4,
+             BH * 512, BH * 512, BH * 512, BH * splits * 128 * 12]
+    assert (L.n_pad, L.code_row_bytes, L.q_scale_count, L.k_scale_count, L.stats_splits) == (npad, crb, qsc, ksc, splits)
+    assert L.total == sum(_round(s, 256) for s in sizes)
+    assert qs.qsdpa_workspace_bytes(p) == L.total
+    offs = [L.q_codes, L.k_codes, L.v_codes, L.q_scales, L.k_scales, L.k_mean, L.v_scales, L.v_amax, L.stats]
+    for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [L.total]):
+        assert o % 256 == 0 and o + s <= o2
+    # FP8 halves the bf16 bytes of Q, K and V; FP4 Q/K codes (V stays FP8) cut them 3x
+    qkv_bf16 = 3 * BH * N * 128 * 2
+    codes = sizes[0] + sizes[1] + sizes[2]
+    if N % 128 == 0:
+        assert codes * (2 if fmt == "fp8" else 3) == qkv_bf16
+
+
+def test_buffer_checks_before_any_launch():
+    lib = qs.load()
+    p = qs.make_params(1, 2, 320)
+    need = qs.qsdpa_workspace_bytes(p)
+    t = 2 * 320 * 128 * 2
+    ok = dict(q=0x10000000, k=0x20000000, v=0x30000000, o=0x40000000, ws=0x50000000, n=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.qsdpa_forward(ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["ws"], a["n"], None)
+
+    assert call(q=None) == qs.QSDPA_ERR_INVALID_ARG
+    assert call(ws=None) == qs.QSDPA_ERR_INVALID_ARG
+    assert call(q=0x10000008) == qs.QSDPA_ERR_ALIGNMENT
+    assert call(o=0x40000004) == qs.QSDPA_ERR_ALIGNMENT
+    assert call(ws=0x50000010) == qs.QSDPA_ERR_ALIGNMENT
+    assert call(n=need - 1) == qs.QSDPA_ERR_WORKSPACE_TOO_SMALL
+    assert call(o=0x10000000 + t - 16) == qs.QSDPA_ERR_ALIAS
+    assert call(o=0x50000000 + need - 256) == qs.QSDPA_ERR_ALIAS
+    assert call(v=0x50000000 - t + 16) == qs.QSDPA_ERR_ALIAS
+    assert lib.qsdpa_attention(ctypes.byref(p), 0x50000000, need - 1, 0x40000000, None) == \
+        qs.QSDPA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.qsdpa_quantize(ctypes.byref(p), 0x10000000, None, 0x30000000, 0x50000000, need, None) == \
+        qs.QSDPA_ERR_INVALID_ARG
+    assert lib.qsdpa_workspace_layout(ctypes.byref(p), None) == qs.QSDPA_ERR_INVALID_ARG

@@ -1,0 +1,152 @@
+"""GPU parity of qsdpa_forward against the oracle: max-abs <= 1e-2 and
+mean-abs <= 1e-3 on the bf16 output, at the full sizes of every workload (the
+oracle evaluates sampled heads and query rows, each row independently), plus
+ragged lengths, closed forms, determinism and out-of-bounds guards."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_attention_qsdpa_amd as qs
+from gpu_helpers import from_dev, run_forward, to_dev
+from workloads import TAU, WORKLOADS, draw
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+# P codes whose fp64 weight lies within this relative distance of an E4M3
+# rounding midpoint may round either way in the kernel's fp32 softmax (logits
+# carry a few fp32 roundings of up to |s c| ~ 64, i.e. ~2e-5 relative in p):
+# either code is correct there, and the oracle bounds their effect on O.
+AMBIGUITY = 2.0 ** -13
+
+
+def sample_rows(N, rng):
+    rows = set(range(min(N, 128)))
+    rows |= set(range(max(0, N - 128), N))
+    if N > 256:
+        mid = (N // 2) // 128 * 128
+        rows |= set(range(mid, mid + 128))
+        rows |= set(rng.choice(N, 64, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def compare(out_bits, qb, kb, vb, fmt, block_q, heads, rows_of, label):
+    errs, raw_errs, exact_errs = [], [], []
+    for b, h in heads:
+        rows = rows_of(b, h)
+        z = oracle.quantize(qb[b:b + 1, h:h + 1], kb[b:b + 1, h:h + 1], vb[b:b + 1, h:h + 1],
+                            fmt=fmt, block_q=block_q, block_k=64)
+        want, bound = oracle.attend(z, TAU, 0, 0, rows, ambiguity=AMBIGUITY)
+        got = oracle.bf16_bits_to_f64(out_bits[b, h, rows])
+        raw = np.abs(got - want)
+        raw_errs.append(raw)
+        errs.append(np.maximum(raw - bound, 0.0))
+        q, k, v = (oracle.bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb))
+        exact_errs.append(np.abs(got - oracle.exact_attention(q, k, v, TAU, rows)))
+    e = np.concatenate([x.ravel() for x in errs])
+    x = np.concatenate([x.ravel() for x in exact_errs])
+    rw = np.concatenate([x.ravel() for x in raw_errs])
+    print(f"[forward] {label}: vs oracle max {e.max():.3e} mean {e.mean():.3e} (raw max {rw.max():.3e} "
+          f"mean {rw.mean():.3e}) | vs exact fp64 max {x.max():.3e} mean {x.mean():.3e}", flush=True)
+    assert np.all(np.isfinite(e))
+    assert e.max() <= MAX_ABS, f"{label}: max-abs {e.max()}"
+    assert e.mean() <= MEAN_ABS, f"{label}: mean-abs {e.mean()}"
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_forward_full_size(gpu_lib, name):
+    w = WORKLOADS[name]
+    qb, kb, vb = draw(w)
+    params = qs.make_params(w.batch, w.heads, w.seq_len, fmt=w.fmt, block_q=w.block_q, block_k=w.block_k)
+    print(f"[forward] start {name} B={w.batch} H={w.heads} N={w.seq_len} fmt={w.fmt}", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    rng = np.random.default_rng(w.wid)
+    if w.batch * w.heads <= 4:
+        heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+        rows_of = lambda b, h: np.arange(w.seq_len)
+    else:
+        heads = sorted({(0, 0), (w.batch - 1, w.heads - 1), (w.batch // 2, 7)})
+        rows_of = lambda b, h: sample_rows(w.seq_len, rng)
+    compare(out, qb, kb, vb, w.fmt, w.block_q, heads, rows_of, name)
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 100, 127, 129, 1000])
+@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128)])
+def test_forward_ragged_lengths(gpu_lib, N, fmt, bq):
+    qb, kb, vb = draw(WORKLOADS["tiny"], batch=2, heads=1, seq_len=N, seed=500 + N)
+    params = qs.make_params(2, 1, N, fmt=fmt, block_q=bq)
+    print(f"[forward] ragged N={N} fmt={fmt} bq={bq}", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    compare(out, qb, kb, vb, fmt, bq, [(0, 0), (1, 0)], lambda b, h: np.arange(N), f"N={N} {fmt} bq={bq}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_zero_queries_closed_form(gpu_lib, fmt):
+    """Q = 0: O is the mean of the dequantized V codes (every P code is 448)."""
+    N = 1000
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=1, seq_len=N, seed=9)
+    qb = np.zeros_like(qb)
+    params = qs.make_params(1, 1, N, fmt=fmt)
+    out = run_forward(qb, kb, vb, params)
+    z = oracle.quantize(qb, kb, vb, fmt=fmt)
+    mean_v = oracle.decode(z.v_codes[0, 0], oracle.E4M3).mean(axis=0) * z.v_scales[0, 0].astype(np.float64)
+    want = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(mean_v))
+    got = oracle.bf16_bits_to_f64(out[0, 0])
+    assert np.max(np.abs(got - want[None, :])) <= 2.0 ** -8 * np.abs(want).max()
+
+
+def test_constant_values_stay_constant(gpu_lib):
+    """V = c per channel: O/c = sum(P)/(448 l) within the E4M3 weight bound."""
+    N = 2000
+    qb, kb, _ = draw(WORKLOADS["tiny"], heads=1, seq_len=N, seed=11)
+    c = np.linspace(0.5, 3.0, 128).astype(np.float32)
+    from workloads import to_bf16_bits
+    vb = to_bf16_bits(np.broadcast_to(c, (1, 1, N, 128)).copy())
+    out = run_forward(qb, kb, vb, qs.make_params(1, 1, N))
+    cv = oracle.bf16_bits_to_f64(vb)[0, 0, 0]
+    rel = np.abs(oracle.bf16_bits_to_f64(out[0, 0]) / cv - 1)
+    assert rel.max() <= 2.0 ** -4 + N * 2.0 ** -10 / 448 + 2.0 ** -8
+
+
+def test_deterministic_and_in_bounds(gpu_lib):
+    """Bitwise-identical repeats; nothing written outside O or the workspace."""
+    w = WORKLOADS["tiny"]
+    N = 1000
+    qb, kb, vb = draw(w, batch=1, heads=3, seq_len=N, seed=21)
+    params = qs.make_params(1, 3, N)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    numel = 3 * N * 128
+    guard = 4096
+    obig = torch.full((numel + 2 * guard,), 1234, dtype=torch.int16, device="cuda")
+    need = qs.qsdpa_workspace_bytes(params)
+    wbig = torch.full((need + 2 * 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    o = obig[guard:guard + numel].view(torch.bfloat16).view(1, 3, N, 128)
+    ws = wbig[4096:4096 + need]
+    outs = []
+    for _ in range(5):
+        qs.qsdpa_forward(q, k, v, out=o, workspace=ws, params=params)
+        torch.cuda.synchronize()
+        outs.append(from_dev(o).copy())
+    for x in outs[1:]:
+        assert np.array_equal(x, outs[0])
+    assert torch.all(obig[:guard] == 1234) and torch.all(obig[guard + numel:] == 1234)
+    assert torch.all(wbig[:4096] == 0x5A) and torch.all(wbig[4096 + need:] == 0x5A)
+
+
+def test_split_calls_equal_forward(gpu_lib):
+    """qsdpa_quantize + qsdpa_attention on a stream equals qsdpa_forward."""
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=777, seed=31)
+    params = qs.make_params(1, 2, 777)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    ref = qs.qsdpa_forward(q, k, v, params=params)
+    s = torch.cuda.Stream()
+    ws = qs.empty_workspace(params)
+    o = torch.empty_like(q)
+    with torch.cuda.stream(s):
+        qs.qsdpa_quantize(q, k, v, ws, params, stream=s)
+        qs.qsdpa_attention(ws, o, params, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16))

@@ -1,0 +1,68 @@
+"""GPU parity of the quantize step: codes, scales and statistics are compared
+bit for bit with the oracle, at the full sizes of every workload (the oracle
+evaluates sampled (b, h) pairs: every (b, h) is quantized independently)."""
+import numpy as np
+import pytest
+
+import oracle
+import precision_attention_qsdpa_amd as qs
+from gpu_helpers import read_workspace, run_quantize
+from workloads import WORKLOADS, draw
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_heads(w):
+    if w.batch * w.heads <= 4:
+        return [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    return sorted({(0, 0), (w.batch - 1, w.heads - 1), (w.batch // 2, w.heads // 2)})
+
+
+def check_quantize(qb, kb, vb, fmt, block_q, heads, label):
+    B, H, N, _ = qb.shape
+    params = qs.make_params(B, H, N, fmt=fmt, block_q=block_q)
+    print(f"[quantize] {label} B={B} H={H} N={N} fmt={fmt} bq={block_q}", flush=True)
+    ws = run_quantize(qb, kb, vb, params)
+    got = read_workspace(ws, params, N)
+    for b, h in heads:
+        z = oracle.quantize(qb[b:b + 1, h:h + 1], kb[b:b + 1, h:h + 1], vb[b:b + 1, h:h + 1],
+                            fmt=fmt, block_q=block_q, block_k=64)
+        for name, want in (("q_codes", z.q_codes), ("k_codes", z.k_codes), ("v_codes", z.v_codes),
+                           ("q_scales", z.q_scales), ("k_scales", z.k_scales), ("k_mean", z.k_mean),
+                           ("v_scales", z.v_scales), ("v_amax", z.v_amax)):
+            g = got[name][b:b + 1, h:h + 1]
+            assert g.shape == want.shape, (name, g.shape, want.shape)
+            if g.dtype == np.float32:
+                ok = np.array_equal(g.view(np.uint32), want.astype(np.float32).view(np.uint32))
+            else:
+                ok = np.array_equal(g, want)
+            if not ok:
+                bad = np.argwhere(g.reshape(want.shape) != want)
+                pytest.fail(f"{label} {name} (b={b},h={h}): {len(bad)} mismatches, first at {bad[:3].tolist()}")
+    for name in ("q_codes_pad", "k_codes_pad", "v_codes_pad", "q_scales_pad", "k_scales_pad"):
+        if name in got:
+            assert not np.any(got[name]), f"{label}: {name} not zero"
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_quantize_bit_exact_full_size(gpu_lib, name):
+    w = WORKLOADS[name]
+    qb, kb, vb = draw(w)
+    check_quantize(qb, kb, vb, w.fmt, w.block_q, sample_heads(w), name)
+
+
+@pytest.mark.parametrize("N", [1, 63, 65, 100, 129, 1000])
+@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128)])
+def test_quantize_ragged_lengths(gpu_lib, N, fmt, bq):
+    qb, kb, vb = draw(WORKLOADS["tiny"], batch=2, heads=2, seq_len=N, seed=77 + N)
+    check_quantize(qb, kb, vb, fmt, bq, [(b, h) for b in range(2) for h in range(2)], f"N={N}")
+
+
+def test_quantize_zero_blocks(gpu_lib):
+    """All-zero Q blocks and a zero V channel: zero scales and codes."""
+    qb, kb, vb = draw(WORKLOADS["tiny"], seq_len=300, seed=5)
+    qb = qb.copy(); vb = vb.copy()
+    qb[:, :, 64:128] = 0
+    vb[:, :, :, 5] = 0
+    for fmt in ("fp8", "fp4"):
+        check_quantize(qb, kb, vb, fmt, 64, [(0, 0), (0, 1)], f"zero-{fmt}")

@@ -37,13 +37,13 @@ def test_online_softmax_without_quantizers_is_exact_softmax(step):
     R, N, D = 9, 300, 16
     S = rng.standard_normal((R, N)) * 3
     V = rng.standard_normal((N, D))
-    acc, l = oracle.online_softmax_av(S, V, step=step, quantize_p=False)
+    acc, l, _ = oracle.online_softmax_av(S, V, step=step, quantize_p=False)
     got = acc / (oracle.P_SCALE * l)[:, None]
     w = np.exp(S - S.max(axis=1, keepdims=True))
     want = (w / w.sum(axis=1, keepdims=True)) @ V
     assert np.max(np.abs(got - want)) <= 1e-12
     # the weights p/l sum to one
-    acc1, l1 = oracle.online_softmax_av(S, np.ones((N, 1)), step=step, quantize_p=False)
+    acc1, l1, _ = oracle.online_softmax_av(S, np.ones((N, 1)), step=step, quantize_p=False)
     assert np.max(np.abs(acc1[:, 0] / (oracle.P_SCALE * l1) - 1)) <= 1e-14
 
 
@@ -61,7 +61,7 @@ def test_worked_example_one_step():
     unquantized p (1.3); O = (448*1 + 128*2) / (448 * 1.3)."""
     S = np.array([[0.0, math.log(0.3)]])
     V = np.array([[1.0], [2.0]])
-    acc, l = oracle.online_softmax_av(S, V, step=64)
+    acc, l, _ = oracle.online_softmax_av(S, V, step=64)
     assert acc[0, 0] == 448 + 128 * 2
     assert abs(l[0] - 1.3) < 1e-15
     assert abs(acc[0, 0] / (448 * l[0]) - 704 / (448 * 1.3)) < 1e-15
@@ -74,9 +74,9 @@ def test_worked_example_step_size_changes_codes():
     S = np.array([[0.0, 2.0]])
     V = np.array([[1.0], [3.0]])
     e2 = math.exp(-2.0)
-    acc1, l1 = oracle.online_softmax_av(S, V, step=1)
+    acc1, l1, _ = oracle.online_softmax_av(S, V, step=1)
     assert abs(acc1[0, 0] - (e2 * 448 + 448 * 3)) < 1e-12 and abs(l1[0] - (1 + e2)) < 1e-15
-    acc2, l2 = oracle.online_softmax_av(S, V, step=2)
+    acc2, l2, _ = oracle.online_softmax_av(S, V, step=2)
     assert acc2[0, 0] == 60 + 448 * 3 and abs(l2[0] - (1 + e2)) < 1e-15
 
 
@@ -164,3 +164,19 @@ def test_forward_close_to_exact_attention_tiny():
     ex = np.stack([oracle.exact_attention(q[0, h], k[0, h], v[0, h], TAU) for h in range(2)])[None]
     err = np.abs(o - ex)
     assert err.max() < 0.1 and err.mean() < 0.01
+
+
+def test_ambiguity_bound_covers_flipped_codes():
+    """A weight placed on an E4M3 midpoint (448 p = 432, between 416 and 448)
+    is ambiguous: the bound equals the code gap times |V| / (448 l), and
+    flipping that one code moves O by exactly the bound."""
+    p_mid = 432.0 / 448.0
+    S = np.array([[0.0, math.log(p_mid), math.log(0.1)]])
+    V = np.array([[1.0], [-2.0], [0.5]])
+    acc, l, amb = oracle.online_softmax_av(S, V, ambiguity=2.0 ** -13)
+    assert amb[0, 0] == 32 * 2.0            # gap 448 - 416, |V| = 2
+    acc0, l0, amb0 = oracle.online_softmax_av(S, V)
+    assert np.all(amb0 == 0) and acc0[0, 0] == acc[0, 0]
+    w_other = 448.0 if oracle.round_to(np.array([432.0]), E4M3)[0] == 416.0 else 416.0
+    flipped = 448 * 1.0 + w_other * -2.0 + oracle.round_to(np.array([44.8]), E4M3)[0] * 0.5
+    assert abs(abs(flipped - acc[0, 0]) - amb[0, 0]) < 1e-12
