@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--workload", default="kontext1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="query rows of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for scaling HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_attn_fp8_kontext1024.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters (if present)")
     return ap.parse_args()
@@ -66,8 +68,17 @@ def main():
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by (batch, head) with no exchange, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 5}))
+        return
 
     import precision_attention_qsdpa_amd as qs
     from workloads import TAU, WORKLOADS, draw

@@ -21,6 +21,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE fp32 division and square root; no contraction unless written out
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=off",
+    # keep the next step's score MFMAs in the block where they are written, so
+    # they interleave with the softmax instead of sinking past its branch
+    "-mllvm", "-disable-machine-sink",
     "-Wall", "-Wno-unused-function",
 ]
 
