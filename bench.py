@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="kontext1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="query rows of the CPU oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="(b,h) pairs of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_attn_fp8_kontext1024.json"),
@@ -39,27 +39,27 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, rows: int):
-    """The oracle, single process with single-threaded BLAS, on one (b, h)
-    and ``rows`` query rows against all keys (quantize of that head included)."""
-    import numpy as np
+def cpu_baseline(w, heads: int):
+    """The oracle, single process with single-threaded BLAS, on the first
+    ``heads`` (b, h) pairs of the workload: quantize of each head and every
+    query row against every key."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     from workloads import TAU, draw
 
-    qb, kb, vb = draw(w, batch=1)
-    qb, kb, vb = qb[:1, :1], kb[:1, :1], vb[:1, :1]
-    rows_idx = np.arange(rows)
+    qb, kb, vb = draw(w, batch=1, heads=heads)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        z = oracle.quantize(qb, kb, vb, fmt=w.fmt, block_q=w.block_q, block_k=w.block_k)
-        oracle.attend(z, TAU, 0, 0, rows_idx)
+        for h in range(heads):
+            z = oracle.quantize(qb[:, h:h + 1], kb[:, h:h + 1], vb[:, h:h + 1], fmt=w.fmt,
+                                block_q=w.block_q, block_k=w.block_k)
+            oracle.attend(z, TAU, 0, 0)
         dt = time.perf_counter() - t0
-    flops = 4.0 * rows * w.seq_len * 128
+    flops = 4.0 * heads * w.seq_len ** 2 * 128
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"(b,h)=(0,0) of {w.name}: quantize of the head + {rows} query rows x {w.seq_len} keys "
-                      f"({dt:.2f} s wall, single-threaded NumPy)"}
+            "sample": f"{heads} of the {w.batch * w.heads} (b,h) pairs of {w.name}, all {w.seq_len} query rows "
+                      f"(quantize + attention), {dt:.1f} s wall, single-threaded NumPy"}
 
 
 def main():
@@ -161,7 +161,7 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     print(json.dumps(rec), flush=True)
 
 
