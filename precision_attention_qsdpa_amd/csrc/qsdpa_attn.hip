@@ -1,4 +1,7 @@
-// Fused flash-style attention over the quantized workspace.
+// Fused flash-style attention over the quantized workspace.  Two kernels:
+// attn_fp8_kernel (FP8 Q/K codes, asynchronous LDS ring) and attn_fp4_kernel
+// (FP4 Q/K codes dequantized to f16 hi/lo pairs).  What follows describes the
+// structure both share.
 //
 // Work split: one workgroup = 4 waves = 128 consecutive queries of one (b,h);
 // each wave owns 32 queries and walks all keys in steps of 64, in ascending
@@ -16,13 +19,13 @@
 // are stored by the quantize step in that same key order, so no shuffle is
 // needed.
 //
-// Pipeline: the score MFMAs of step t+1 are issued before the softmax of
-// step t, so the matrix cores work while the VALU runs the softmax.  K tiles
-// are therefore staged in LDS one step ahead of V tiles: during step t the
-// LDS holds K(t+1) and V(t) while the registers bring in K(t+2) and V(t+1)
-// (two LDS buffers each, one barrier per step).  Tiles are 8 KB with a
-// 16-byte-chunk XOR swizzle that keeps both the 128-bit stores and the
-// 128-bit operand reads free of bank conflicts.
+// Pipeline: step t issues the score MFMAs of step t+1 and the value MFMAs of
+// step t-1 while the VALU runs the softmax of step t, so the matrix cores
+// work beside the softmax in one instruction stream.  The accumulator
+// recursion is the online-softmax one delayed by a step: step t first
+// rescales O^T by alpha(t-1), then accumulates V(t-1)^T P(t-1)^T.  Tiles are
+// 8 KB with a 16-byte-chunk XOR swizzle that keeps both the 128-bit stores and
+// the 128-bit operand reads free of bank conflicts.
 //
 // Numerics: scores are exact integer-valued FP8 dot products accumulated in
 // fp32 by the MFMA; one per-step constant c = tau*log2(e)*sQ*sK turns them
@@ -92,17 +95,338 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
   return xcd * q + min(xcd, rem) + slot;
 }
 
-template <bool FP4>
-__global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
+
+// ---------------------------------------------------------------------------
+// Pieces shared by both kernels
+// ---------------------------------------------------------------------------
+
+// Online softmax of one 64-key step for the 32 raw scores a lane holds (two
+// 16-value accumulator blocks, overwritten by the weights).  c turns a raw
+// score into a base-2 logit.  Returns the FP8 weights E4M3(448 p) packed in
+// B-operand order (slot j = kb*16 + i); updates the running max m and the sum
+// l of the unquantized p; alpha = exp2(m_old - m_new), exactly 1 when the max
+// did not move.  FULL = false masks keys at or past N (the last step).
+template <bool FULL>
+__device__ __forceinline__ v8i softmax_step(v16f* s, float c, float& m, float& l, float& alpha,
+                                            int key0, int N, int g) {
+  float m_new;
+  if constexpr (FULL) {
+    float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) {
+      m0 = fmaxf(fmaxf(m0, s[0][i]), s[0][i + 1]);
+      m1 = fmaxf(fmaxf(m1, s[1][i]), s[1][i + 1]);
+    }
+    const float mx = pair_max(fmaxf(fmaxf(m0, s[0][15]), fmaxf(m1, s[1][15])));
+    m_new = fmaxf(m, c * mx);
+    const float b = LOG2_448 - m_new;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, b));
+  } else {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        s[kb][i] = key < N ? s[kb][i] * c : -INFINITY;
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    m_new = fmaxf(m, pair_max(mx));
+    const float b = LOG2_448 - m_new;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] + b);
+  }
+  v8i pb;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int kb = w >> 2, i0 = 4 * (w & 3);
+    const int x = cvt_e4m3x2<false>(s[kb][i0], s[kb][i0 + 1], undef_int());
+    pb[w] = cvt_e4m3x2<true>(s[kb][i0 + 2], s[kb][i0 + 3], x);
+  }
+  // row sum of the unquantized p (four independent chains)
+  float ps[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+  for (int i = 4; i < 16; ++i) ps[i & 3] += s[0][i];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ps[i & 3] += s[1][i];
+  const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  alpha = m_new != m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+  l = alpha * l + psum;
+  m = m_new;
+  return pb;
+}
+
+// O^T *= alpha, skipped when alpha is exactly 1 in every lane
+__device__ __forceinline__ void rescale_o(v16f* o, float alpha) {
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+  }
+}
+
+// O^T += V^T . P^T for the V^T tile at vbuf (channel rows db*32 + r)
+__device__ __forceinline__ void value_mfma(v16f* o, const v8i& pb, const uint8_t* vbuf, int voff0, int voff1) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const v8i a = lds_v8i(vbuf + db * 2048 + voff0, vbuf + db * 2048 + voff1);
+    o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[db], 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// O = acc * sV / (448 l) as bf16 for query q (one lane pair holds it):
+// each lane stores 16 runs of 4 channels (8 bytes).
+__device__ __forceinline__ void store_out(const v16f* o, float l, uint16_t* __restrict__ out,
+                                          const float* __restrict__ vsc, size_t row, bool valid, int g) {
+  const float inv_l = 1.f / pair_sum(l);
+  if (!valid) return;
+  uint16_t* orow = out + row * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = db * 32 + 8 * rg + 4 * g;
+      const uint32_t b0 = f32_to_bf16(o[db][4 * rg + 0] * (vsc[d0 + 0] * inv_l));
+      const uint32_t b1 = f32_to_bf16(o[db][4 * rg + 1] * (vsc[d0 + 1] * inv_l));
+      const uint32_t b2 = f32_to_bf16(o[db][4 * rg + 2] * (vsc[d0 + 2] * inv_l));
+      const uint32_t b3 = f32_to_bf16(o[db][4 * rg + 3] * (vsc[d0 + 3] * inv_l));
+      *(u32x2*)(orow + d0) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 kernel with asynchronous tile loads.  Same work split, layouts and
+// softmax as attn_kernel, but K and V^T tiles go from HBM/L2 straight into LDS
+// (global_load_lds_dwordx4: no registers, no LDS store instructions) through
+// a ring of 4 stages, issued 3 steps before they are read:
+//   step t reads K(t+1) (scores of step t+1) and V(t-1) (values of step t-1)
+//   and issues the loads of K(t+4) and V(t+2).
+// Each wave issues 4 such loads per step, so at the end of step t a wave waits
+// until at most 8 of its loads are outstanding (those of steps t-1 and t),
+// which means K(t+2) and V(t) have landed, then joins the barrier.  The
+// barrier is a plain s_barrier: the only loads in flight across it are these
+// ring loads, which target stages no wave reads before the wait that covers
+// them.
+// ---------------------------------------------------------------------------
+constexpr int NSTAGE = 4;
+
+// One 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane i
+// reads gbase + voff and the wave writes 64 x 16 contiguous bytes at LDS byte
+// address lds.  Written as one asm statement (M0 set and load issued together)
+// so that no compiler-inserted wait lands between the ring loads; the
+// instruction has no VGPR result, and completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes the stage.  Every global
+// load in the loop is one of these, so the explicit vmcnt counts are exact.
+__device__ __forceinline__ void ring_copy16(const uint8_t* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+// LDS byte address of p, made a wave-uniform (scalar) value for M0
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p);
+}
+
+__device__ __forceinline__ void ring_barrier_wait8() {
+  // s_waitcnt vmcnt(8) lgkmcnt(0): ring copies of the last two steps may stay
+  // in flight; every LDS read of this wave has returned before the barrier,
+  // so a stage can be refilled right after it
+  __builtin_amdgcn_s_waitcnt(0x0070 | 8);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kc,
     const float* __restrict__ ks, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
     uint16_t* __restrict__ out, int N, int n_pad, int block_q, int q_scale_count,
     int k_scale_count, float tau_log2e, int tiles_per_bh) {
-  // K tile in LDS: FP8 codes, or in FP4 mode the dequantized values as an
-  // f16 pair hi + lo (hi = f16(x), lo = f16(x - hi)), which carries x to about
-  // 2^-22 relative so the scores keep fp32-level accuracy.
-  constexpr int KBYTES = FP4 ? 4 * KTILE : KTILE;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KBYTES];
+  // ring: stages 0..3 of K tiles, then stages 0..3 of V^T tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * NSTAGE * KTILE];
+  auto lds_k = [&](int S) -> uint8_t* { return ring + S * KTILE; };
+  auto lds_v = [&](int S) -> uint8_t* { return ring + (NSTAGE + S) * KTILE; };
+  // LDS byte address of the ring and this wave's 2 KB slice of a stage, as scalars
+  const uint32_t ring_lds = lds_addr(ring);
+  const uint32_t wave_lds = ring_lds + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 2048u;
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / tiles_per_bh, tile = wg - bh * tiles_per_bh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+  const int q0 = tile * QT + wave * QW;
+  const int T = (N + KSTEP - 1) / KSTEP;
+
+  v8i qb8[2];
+  {
+    const uint8_t* qrow = qc + ((size_t)bh * n_pad + q0 + r) * D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qb8[h] = lds_v8i(qrow + 64 * h + 32 * g, qrow + 64 * h + 32 * g + 16);
+  }
+  const float cscale = tau_log2e * qs[(size_t)bh * q_scale_count + q0 / block_q];
+  const uint8_t* kbase = kc + (size_t)bh * n_pad * D;
+  const float* ksc = ks + (size_t)bh * k_scale_count;
+  const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
+
+  // K operand chunks (row kb*32 + r, chunk 4h + 2g + i): the swizzle of row
+  // kb*32 + r is that of row r with bit 2 flipped by kb, so
+  // offset(kb, h, i) = kb * 4096 + offset(0, h ^ kb, i).
+  int koff0[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) koff0[h][i] = k_off(r, 4 * h + 2 * g + i);
+  const int voff0 = v_off(r, 2 * g), voff1 = v_off(r, 2 * g + 1);
+
+  // Ring loads: wave w's instruction i fills LDS chunks (2w+i)*64 + lane of a
+  // stage; each lane fetches the global chunk the swizzle puts there.
+  uint32_t kg[2], vg[2];   // unsigned: lets the loads use an SGPR base + 32-bit offset
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int P = (2 * wave + i) * 64 + lane;
+    const int row = P >> 3, pc = P & 7;
+    kg[i] = (uint32_t)(row * 128 + ((pc ^ ((row ^ (row >> 3)) & 7)) << 4));
+    const int d = P >> 2, pv = P & 3;
+    vg[i] = (uint32_t)(d * 64 + ((pv ^ (((d >> 1) ^ (d >> 3)) & 3)) << 4));
+  }
+  auto ring_k = [&](int t, int S) {
+    const uint8_t* tp = kbase + (size_t)t * KTILE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ring_copy16(tp, kg[i], wave_lds + S * KTILE + i * 1024);
+  };
+  auto ring_v = [&](int t, int S) {
+    const uint8_t* tp = vbase + (size_t)t * KTILE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], wave_lds + (NSTAGE + S) * KTILE + i * 1024);
+  };
+
+  auto scores = [&](const uint8_t* kbuf, v16f* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = v16f{};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v8i a = lds_v8i(kbuf + kb * 4096 + koff0[h ^ kb][0], kbuf + kb * 4096 + koff0[h ^ kb][1]);
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb8[h], s[kb], 0, 0, 0, 127, 0, 127);
+      }
+    }
+  };
+  v16f o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = v16f{};
+  float m = -INFINITY, l = 0.f;
+
+  auto softmax = [&](int t, v16f* s, auto full_t, float& alpha) -> v8i {
+    return softmax_step<decltype(full_t)::value>(s, cscale * ksc[t], m, l, alpha, t * KSTEP, N, g);
+  };
+  auto rescale = [&](float alpha) { rescale_o(o, alpha); };
+  auto pv = [&](const v8i& pb, const uint8_t* vbuf) { value_mfma(o, pb, vbuf, voff0, voff1); };
+
+  // prologue: K(0..3) and V(0), V(1) in flight; V(-1) (stage 3) is zero.
+  // The Q operand and scale loads complete first, so that from here on the
+  // only vector-memory loads in flight are ring copies.
+  const int Tm1 = T - 1;
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+  ring_k(0, 0);
+  ring_k(min(1, Tm1), 1);
+  ring_k(min(2, Tm1), 2);
+  ring_k(min(3, Tm1), 3);
+  ring_v(0, 0);
+  ring_v(min(1, Tm1), 1);
+  *(u32x4*)(lds_v(3) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+  *(u32x4*)(lds_v(3) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
+  // K(0), K(1) landed (at most K(2), K(3), V(0), V(1) outstanding)
+  __builtin_amdgcn_s_waitcnt(0x0070 | 8);
+  asm volatile("s_barrier" ::: "memory");
+  v16f sa[2], sb[2];
+  scores(lds_k(0), sa);
+  v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  float alpha_prev = 1.f;
+
+  // steps 0 .. T-2 (full)
+  auto step = [&](int t, v16f* s_cur, v16f* s_next, auto st) {
+    constexpr int S = decltype(st)::value;   // t % 4
+    rescale(alpha_prev);
+    ring_k(min(t + 4, Tm1), S);
+    ring_v(min(t + 2, Tm1), (S + 2) & 3);
+    scores(lds_k((S + 1) & 3), s_next);
+    pv(pb_prev, lds_v((S + 3) & 3));
+    pb_prev = softmax(t, s_cur, std::true_type{}, alpha_prev);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
+    }
+    ring_barrier_wait8();
+  };
+  int t = 0;
+  for (; t + 4 < T; t += 4) {
+    step(t, sa, sb, std::integral_constant<int, 0>{});
+    step(t + 1, sb, sa, std::integral_constant<int, 1>{});
+    step(t + 2, sa, sb, std::integral_constant<int, 2>{});
+    step(t + 3, sb, sa, std::integral_constant<int, 3>{});
+  }
+  // remaining full steps t .. T-2 (at most 3; t is a multiple of 4 here, so
+  // the ring stage is t & 3 computed at run time), then the last step T-1
+  auto step_dyn = [&](int tt, v16f* s_cur, v16f* s_next) {
+    const int S = tt & 3;
+    rescale(alpha_prev);
+    ring_k(min(tt + 4, Tm1), S);
+    ring_v(min(tt + 2, Tm1), (S + 2) & 3);
+    scores(lds_k((S + 1) & 3), s_next);
+    pv(pb_prev, lds_v((S + 3) & 3));
+    pb_prev = softmax(tt, s_cur, std::true_type{}, alpha_prev);
+    ring_barrier_wait8();
+  };
+  auto last = [&](int tl, v16f* s_cur) {
+    const int S = tl & 3;
+    rescale(alpha_prev);
+    pv(pb_prev, lds_v((S + 3) & 3));
+    float alpha;
+    const v8i pb = (tl + 1) * KSTEP <= N ? softmax(tl, s_cur, std::true_type{}, alpha)
+                                         : softmax(tl, s_cur, std::false_type{}, alpha);
+    // V(tl) is in stage S (issued at step tl-2 or in the prologue): wait for every ring copy
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+    rescale(alpha);
+    pv(pb, lds_v(S));
+  };
+  for (; t + 2 < T; t += 2) {
+    step_dyn(t, sa, sb);
+    step_dyn(t + 1, sb, sa);
+  }
+  if (t + 1 < T) {
+    step_dyn(t, sa, sb);
+    last(t + 1, sb);
+  } else {
+    last(t, sa);
+  }
+
+  const int q = q0 + r;
+  store_out(o, l, out, vs + (size_t)bh * D, (size_t)bh * N + q, q < N, g);
+}
+
+// ---------------------------------------------------------------------------
+// FP4 kernel: Q and K arrive as E2M1 codes with an fp32 scale per 16
+// channels.  Q is dequantized once into registers and each K tile once per
+// workgroup into LDS, both as f16 pairs hi = f16(x), lo = f16(x - hi), which
+// carry x to about 2^-22 relative; the scores are three f16 MFMAs per
+// 16-channel chunk (hi.hi + lo.hi + hi.lo), so they keep fp32-level accuracy
+// while P and V stay FP8.  Tiles are staged through registers (the K tile is
+// expanded 4x on the way); during step t the LDS holds K(t+1) and V(t-1)
+// and the registers bring in K(t+2) and V(t) (two buffers each, one barrier
+// per step).  One wave per SIMD: the f16 operands need more registers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
+    const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kc,
+    const float* __restrict__ ks, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
+    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][4 * KTILE];   // hi tile, then lo tile
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][KTILE];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -111,16 +435,9 @@ __global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
   const int q0 = tile * QT + wave * QW;
   const int T = (N + KSTEP - 1) / KSTEP;
 
-  // ---- Q operand (B side of S^T), held in registers for the whole kernel.
-  v8i qb8[2];
+  // Q operand: chunk c covers channels 16c + 8g .. 16c + 8g + 7 of query q0 + r
   v8h qhi[8], qlo[8];
-  float cscale;   // base-2 logit per unit of the raw MFMA score
-  if constexpr (!FP4) {
-    const uint8_t* qrow = qc + ((size_t)bh * n_pad + q0 + r) * D;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) qb8[h] = lds_v8i(qrow + 64 * h + 32 * g, qrow + 64 * h + 32 * g + 16);
-    cscale = tau_log2e * qs[(size_t)bh * q_scale_count + q0 / block_q];
-  } else {
+  {
     const size_t qrow = (size_t)bh * n_pad + q0 + r;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -133,47 +450,26 @@ __global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
         qlo[c][e] = (_Float16)(x - (float)qhi[c][e]);
       }
     }
-    cscale = tau_log2e;
   }
-
-  const uint8_t* kbase = FP4 ? kc + (size_t)bh * n_pad * 64 : kc + (size_t)bh * n_pad * D;
-  const float* ksc = FP4 ? ks + (size_t)bh * n_pad * 8 : ks + (size_t)bh * k_scale_count;
+  const uint8_t* kbase = kc + (size_t)bh * n_pad * 64;
+  const float* ksc = ks + (size_t)bh * n_pad * 8;
   const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
-
-  // ---- per-lane LDS offsets, computed once
-  // K operand chunks of this lane: row kb*32 + r, chunks 4h + 2g + i.
-  int koff[2][2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) koff[kb][h][i] = k_off(kb * 32 + r, 4 * h + 2 * g + i);
-  // V operand chunks: channel row db*32 + r (the swizzle does not depend on db).
   const int voff0 = v_off(r, 2 * g), voff1 = v_off(r, 2 * g + 1);
-  // staging stores of this thread: chunks tid and tid + 256
-  const int kst0 = k_off(tid >> 3, tid & 7), kst1 = k_off((tid + 256) >> 3, tid & 7);
   const int vst0 = v_off(tid >> 2, tid & 3), vst1 = v_off((tid + 256) >> 2, tid & 3);
 
-  // ---- tile staging: global -> registers -> LDS
-  u32x4 kreg[2], vreg[2];
+  // staging: this thread handles (key, 16-channel group) pairs tid and tid + 256
   uint32_t kcode[2][2];
   float kscl[2];
+  u32x4 vreg[2];
   auto load_k = [&](int t) {
-    if constexpr (!FP4) {
-      const uint8_t* tp = kbase + (size_t)t * KTILE;
-      kreg[0] = *(const u32x4*)(tp + tid * 16);
-      kreg[1] = *(const u32x4*)(tp + tid * 16 + 4096);
-    } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ci = tid + 256 * i;
-        const int key = ci >> 3, grp = ci & 7;
-        const u32x2 w = *(const u32x2*)(kbase + ((size_t)t * KSTEP + key) * 64 + grp * 8);
-        kcode[i][0] = w[0];
-        kcode[i][1] = w[1];
-        kscl[i] = ksc[((size_t)t * KSTEP + key) * 8 + grp];
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + 256 * i;
+      const int key = ci >> 3, grp = ci & 7;
+      const u32x2 w = *(const u32x2*)(kbase + ((size_t)t * KSTEP + key) * 64 + grp * 8);
+      kcode[i][0] = w[0];
+      kcode[i][1] = w[1];
+      kscl[i] = ksc[((size_t)t * KSTEP + key) * 8 + grp];
     }
   };
   auto load_v = [&](int t) {
@@ -182,26 +478,21 @@ __global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
     vreg[1] = *(const u32x4*)(tp + tid * 16 + 4096);
   };
   auto store_k = [&](uint8_t* kbuf) {
-    if constexpr (!FP4) {
-      *(u32x4*)(kbuf + kst0) = kreg[0];
-      *(u32x4*)(kbuf + kst1) = kreg[1];
-    } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ci = tid + 256 * i;
-        const int key = ci >> 3, grp = ci & 7;
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + 256 * i;
+      const int key = ci >> 3, grp = ci & 7;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          v8h hv, lv;
+      for (int half = 0; half < 2; ++half) {
+        v8h hv, lv;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = e2m1_value((kcode[i][half] >> (4 * e)) & 15u) * kscl[i];
-            hv[e] = (_Float16)x;
-            lv[e] = (_Float16)(x - (float)hv[e]);
-          }
-          *(v8h*)(kbuf + kh_off(key, 2 * grp + half)) = hv;
-          *(v8h*)(kbuf + 2 * KTILE + kh_off(key, 2 * grp + half)) = lv;
+        for (int e = 0; e < 8; ++e) {
+          const float x = e2m1_value((kcode[i][half] >> (4 * e)) & 15u) * kscl[i];
+          hv[e] = (_Float16)x;
+          lv[e] = (_Float16)(x - (float)hv[e]);
         }
+        *(v8h*)(kbuf + kh_off(key, 2 * grp + half)) = hv;
+        *(v8h*)(kbuf + 2 * KTILE + kh_off(key, 2 * grp + half)) = lv;
       }
     }
   };
@@ -209,28 +500,18 @@ __global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
     *(u32x4*)(vbuf + vst0) = vreg[0];
     *(u32x4*)(vbuf + vst1) = vreg[1];
   };
-
-  // ---- S^T = K . Q^T for the two 32-key blocks of a step, from a K buffer
   auto scores = [&](const uint8_t* kbuf, v16f* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = v16f{};
-      if constexpr (!FP4) {
+      const int row = kb * 32 + r;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const v8i a = lds_v8i(kbuf + koff[kb][h][0], kbuf + koff[kb][h][1]);
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb8[h], s[kb], 0, 0, 0, 127, 0, 127);
-        }
-      } else {
-        const int row = kb * 32 + r;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const v8h ah = *(const v8h*)(kbuf + kh_off(row, 2 * c + g));
-          const v8h al = *(const v8h*)(kbuf + 2 * KTILE + kh_off(row, 2 * c + g));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qhi[c], s[kb], 0, 0, 0);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qhi[c], s[kb], 0, 0, 0);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qlo[c], s[kb], 0, 0, 0);
-        }
+      for (int c = 0; c < 8; ++c) {
+        const v8h ah = *(const v8h*)(kbuf + kh_off(row, 2 * c + g));
+        const v8h al = *(const v8h*)(kbuf + 2 * KTILE + kh_off(row, 2 * c + g));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qhi[c], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qhi[c], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qlo[c], s[kb], 0, 0, 0);
       }
     }
   };
@@ -240,97 +521,14 @@ __global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
   for (int i = 0; i < 4; ++i) o[i] = v16f{};
   float m = -INFINITY, l = 0.f;
 
-  // ---- online softmax of one step on scores s (step t): returns the packed
-  // FP8 weights and the rescale factor; updates m and l.
-  auto softmax = [&](int t, v16f* s, auto full_t, float& alpha) -> v8i {
-    constexpr bool full = decltype(full_t)::value;
-    const float c = FP4 ? cscale : cscale * ksc[t];
-    float m_new;
-    if constexpr (full) {
-      // max over the 32 raw scores of this lane (two independent chains)
-      float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-      float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
-#pragma unroll
-      for (int i = 3; i < 15; i += 2) {
-        m0 = fmaxf(fmaxf(m0, s[0][i]), s[0][i + 1]);
-        m1 = fmaxf(fmaxf(m1, s[1][i]), s[1][i + 1]);
-      }
-      const float mx = pair_max(fmaxf(fmaxf(m0, s[0][15]), fmaxf(m1, s[1][15])));
-      m_new = fmaxf(m, c * mx);
-      const float b = LOG2_448 - m_new;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, b));
-    } else {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t * KSTEP + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          s[kb][i] = key < N ? s[kb][i] * c : -INFINITY;
-          mx = fmaxf(mx, s[kb][i]);
-        }
-      m_new = fmaxf(m, pair_max(mx));
-      const float b = LOG2_448 - m_new;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] + b);
-    }
-    // P -> FP8, packed in the B-operand order (slot j = kb*16 + i)
-    v8i pb;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, i0 = 4 * (w & 3);
-      const int x = cvt_e4m3x2<false>(s[kb][i0], s[kb][i0 + 1], undef_int());
-      pb[w] = cvt_e4m3x2<true>(s[kb][i0 + 2], s[kb][i0 + 3], x);
-    }
-    // row sum of the unquantized p (four independent chains)
-    float ps[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
-#pragma unroll
-    for (int i = 4; i < 16; ++i) ps[i & 3] += s[0][i];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ps[i & 3] += s[1][i];
-    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    alpha = m_new != m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-    l = alpha * l + psum;
-    m = m_new;
-    return pb;
-  };
-  // O^T *= alpha, skipped when alpha is exactly 1 in every lane
-  auto rescale = [&](float alpha) {
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
-  };
-  // O^T += V^T . P^T for the V tile in vbuf
-  auto pv = [&](const v8i& pb, const uint8_t* vbuf) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const v8i a = lds_v8i(vbuf + db * 2048 + voff0, vbuf + db * 2048 + voff1);
-      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[db], 0, 0, 0, 127, 0, 127);
-    }
-  };
-
-  // ---- Pipeline.  Step t issues the score MFMAs of step t+1 and the value
-  // MFMAs of step t-1 while the VALU runs the softmax of step t, so the
-  // matrix cores and the VALU work side by side in one instruction stream.
-  // During step t the LDS holds K(t+1) and V(t-1); the registers bring in
-  // K(t+2) and V(t), stored at the end of the step (two buffers each).
-  // Order on O^T: step t first rescales by alpha(t-1), then accumulates
-  // PV(t-1), which is the online-softmax recursion delayed by one step.
+  // prologue: K(0), K(1) in LDS; V buffer 1 (read by the zero-weight value
+  // product of step -1) cleared
   load_k(0);
   store_k(lds_k[0]);
   if (T > 1) {
     load_k(1);
     store_k(lds_k[1]);
   }
-  // V buffer 1 is read by the (zero-weight) value product of step -1
   *(u32x4*)(lds_v[1] + vst0) = u32x4{0u, 0u, 0u, 0u};
   *(u32x4*)(lds_v[1] + vst1) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
@@ -339,23 +537,15 @@ __global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
   v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;
 
-  // steps 0 .. T-2 are full 64-key steps (only the last step can be short)
+  // steps 0 .. T-2 (full)
   auto step = [&](int t, v16f* s_cur, v16f* s_next, auto par) {
     constexpr int P = decltype(par)::value;   // t & 1
-    rescale(alpha_prev);
+    rescale_o(o, alpha_prev);
     load_k(min(t + 2, T - 1));
     load_v(t);
     scores(lds_k[P ^ 1], s_next);
-    pv(pb_prev, lds_v[P ^ 1]);
-    pb_prev = softmax(t, s_cur, std::true_type{}, alpha_prev);
-    if constexpr (!FP4) {
-      // interleave: each MFMA followed by a slice of the softmax VALU work
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
-      }
-    }
+    value_mfma(o, pb_prev, lds_v[P ^ 1], voff0, voff1);
+    pb_prev = softmax_step<true>(s_cur, tau_log2e, m, l, alpha_prev, t * KSTEP, N, g);
     store_k(lds_k[P]);
     store_v(lds_v[P]);
     __syncthreads();
@@ -365,46 +555,30 @@ __global__ __launch_bounds__(256, FP4 ? 1 : 2) void attn_kernel(
     step(t, sa, sb, std::integral_constant<int, 0>{});
     step(t + 1, sb, sa, std::integral_constant<int, 1>{});
   }
-  // last one or two steps
+  // the last step T-1 (possibly short)
   auto last = [&](int tl, v16f* s_cur, auto par) {
     constexpr int P = decltype(par)::value;
-    rescale(alpha_prev);
+    rescale_o(o, alpha_prev);
     load_v(tl);
-    pv(pb_prev, lds_v[P ^ 1]);
+    value_mfma(o, pb_prev, lds_v[P ^ 1], voff0, voff1);
     float alpha;
-    const v8i pb = (tl + 1) * KSTEP <= N ? softmax(tl, s_cur, std::true_type{}, alpha)
-                                         : softmax(tl, s_cur, std::false_type{}, alpha);
+    const v8i pb = (tl + 1) * KSTEP <= N
+                       ? softmax_step<true>(s_cur, tau_log2e, m, l, alpha, tl * KSTEP, N, g)
+                       : softmax_step<false>(s_cur, tau_log2e, m, l, alpha, tl * KSTEP, N, g);
     store_v(lds_v[P]);
     __syncthreads();
-    rescale(alpha);
-    pv(pb, lds_v[P]);
+    rescale_o(o, alpha);
+    value_mfma(o, pb, lds_v[P], voff0, voff1);
   };
-  if (t + 1 < T) {           // two steps left: t (full) and t+1 (last)
+  if (t + 1 < T) {
     step(t, sa, sb, std::integral_constant<int, 0>{});
     last(t + 1, sb, std::integral_constant<int, 1>{});
-  } else {                   // one step left: t (last)
+  } else {
     last(t, sa, std::integral_constant<int, 0>{});
   }
 
-  // ---- epilogue: O = acc * sV / (448 l), bf16, 4 channels (8 bytes) per store
-  const float ltot = pair_sum(l);
-  const float inv_l = 1.f / ltot;
   const int q = q0 + r;
-  if (q < N) {
-    uint16_t* orow = out + ((size_t)bh * N + q) * D;
-    const float* vsc = vs + (size_t)bh * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = db * 32 + 8 * rg + 4 * g;
-        const uint32_t b0 = f32_to_bf16(o[db][4 * rg + 0] * (vsc[d0 + 0] * inv_l));
-        const uint32_t b1 = f32_to_bf16(o[db][4 * rg + 1] * (vsc[d0 + 1] * inv_l));
-        const uint32_t b2 = f32_to_bf16(o[db][4 * rg + 2] * (vsc[d0 + 2] * inv_l));
-        const uint32_t b3 = f32_to_bf16(o[db][4 * rg + 3] * (vsc[d0 + 3] * inv_l));
-        *(u32x2*)(orow + d0) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-      }
-  }
+  store_out(o, l, out, vs + (size_t)bh * D, (size_t)bh * N + q, q < N, g);
 }
 
 void launch_attention(const LaunchArgs& a, hipStream_t s) {
@@ -412,13 +586,12 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
   const int tiles = a.n_pad / QT;
   const float tl = a.softmax_scale * LOG2E;
   if (a.fp4) {
-    attn_kernel<true><<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes,
-                                                  a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,
-                                                  a.q_scale_count, a.k_scale_count, tl, tiles);
+    attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes,
+                                                a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles);
   } else {
-    attn_kernel<false><<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes,
-                                                   a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,
-                                                   a.q_scale_count, a.k_scale_count, tl, tiles);
+    attn_fp8_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes,
+                                                a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,
+                                                a.q_scale_count, a.k_scale_count, tl, tiles);
   }
 }
 
