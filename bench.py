@@ -152,7 +152,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
                    "head_dim": 128, "qk_format": w.fmt, "block_q": w.block_q, "block_k": w.block_k,
                    "pct_fp8_peak": round(100.0 * tflops / FP8_PEAK_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel<fp8>", "achieved": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
         "quantize": {"ms_per_launch": round(ms_quant, 4),

@@ -59,15 +59,28 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
 
 // Pass 2: per (b,h), combine the ranges: mu = fp32(fp64 sum / N),
 // vmax = max, sV = fp32(vmax / 448).  grid = BH, block = 128 (one channel each).
+// The partial sums are fetched eight at a time (independent loads) and added
+// in range order.
 __global__ __launch_bounds__(128) void stats_final_kernel(
     const double* __restrict__ psum, const float* __restrict__ pmax, int N, int splits,
     float* __restrict__ mu, float* __restrict__ vamax, float* __restrict__ vscale) {
   const int bh = blockIdx.x, d = threadIdx.x;
+  const double* ps = psum + (size_t)bh * splits * D + d;
+  const float* pm = pmax + (size_t)bh * splits * D + d;
   double t = 0.0;
   float mm = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    t += psum[((size_t)bh * splits + s) * D + d];
-    mm = fmaxf(mm, pmax[((size_t)bh * splits + s) * D + d]);
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    double x[8];
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { x[i] = ps[(s + i) * D]; y[i] = pm[(s + i) * D]; }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { t += x[i]; mm = fmaxf(mm, y[i]); }
+  }
+  for (; s < splits; ++s) {
+    t += ps[s * D];
+    mm = fmaxf(mm, pm[s * D]);
   }
   mu[bh * D + d] = (float)(t / (double)N);
   vamax[bh * D + d] = mm;
@@ -130,24 +143,6 @@ __device__ __forceinline__ void fp8_block(const uint16_t* __restrict__ x, const 
       out[1] = (uint32_t)hi;
     }
     *(u32x2*)(codes + ((size_t)bh * n_pad + n) * D + cg * 8) = out;
-  }
-}
-
-// grid = (q_blocks + k_blocks, BH): the first q_blocks blocks quantize Q
-// (block_q tokens each), the rest quantize smoothed K (64 tokens each).
-template <int BQ>
-__global__ __launch_bounds__(256) void quant_qk_fp8_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
-    uint8_t* __restrict__ qc, float* __restrict__ qs, uint8_t* __restrict__ kc,
-    float* __restrict__ ks, int N, int n_pad) {
-  __shared__ float red[4];
-  const int bh = blockIdx.y;
-  const int qb = n_pad / BQ;
-  const int b = blockIdx.x;
-  if (b < qb) {
-    fp8_block<BQ>(q, nullptr, qc, qs + (size_t)bh * qb, N, n_pad, bh, b, red);
-  } else {
-    fp8_block<KSTEP>(k, mu, kc, ks + (size_t)bh * (n_pad / KSTEP), N, n_pad, bh, b - qb, red);
   }
 }
 
@@ -214,12 +209,18 @@ __device__ __forceinline__ int vtile_pos(int key) {
   return 32 * g + 16 * kb + r;
 }
 
-__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
-                                                      const float* __restrict__ vamax,
-                                                      uint8_t* __restrict__ vc, int N, int n_pad) {
-  __shared__ uint8_t tile[D * KSTEP];
-  const int t = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, cg = tid & 15, rl = tid >> 4;
+// One 64-key V tile.  Thread = (token group tg of 4 consecutive keys, channel
+// group cg of 8): the 4 keys of a group sit in 4 consecutive bytes of a
+// channel row (keys 4m..4m+3 map to bytes p..p+3), so each thread writes one
+// 32-bit word per channel.  The LDS copy of the tile uses 72-byte rows, which
+// keeps those word writes free of bank conflicts; it is then copied out as the
+// 8 KB tile.  Keys at or past N and channels with vmax = 0 get zero codes.
+constexpr int VROW = 72;
+
+__device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, const float* __restrict__ vamax,
+                                             uint8_t* __restrict__ vc, int N, int n_pad, int bh, int t,
+                                             uint8_t* tile) {
+  const int tid = threadIdx.x, tg = tid & 15, cg = tid >> 4;
   float inv[8];
   bool nz[8];
 #pragma unroll
@@ -228,32 +229,67 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     nz[j] = a > 0.f;
     inv[j] = nz[j] ? FP8_MAX / a : 0.f;
   }
+  float val[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int key = rl + 16 * i;
-    const int n = t * KSTEP + key;
-    float val[8];
+    const int n = t * KSTEP + 4 * tg + i;
     if (n < N) {
       const u32x4 w = *(const u32x4*)(v + ((size_t)bh * N + n) * D + cg * 8);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { val[2 * j] = bf16_lo(w[j]); val[2 * j + 1] = bf16_hi(w[j]); }
-    }
-    const int pos = vtile_pos(key);
+      for (int j = 0; j < 4; ++j) { val[i][2 * j] = bf16_lo(w[j]); val[i][2 * j + 1] = bf16_hi(w[j]); }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      int c = 0;
-      if (n < N) c = cvt_e4m3x2<false>(clamp448(val[j] * inv[j]), clamp448(val[j + 1] * inv[j + 1]), 0);
-      const uint32_t c0 = (n < N && nz[j]) ? (uint32_t)(c & 0xff) : 0u;
-      const uint32_t c1 = (n < N && nz[j + 1]) ? (uint32_t)((c >> 8) & 0xff) : 0u;
-      tile[(cg * 8 + j) * KSTEP + pos] = (uint8_t)c0;
-      tile[(cg * 8 + j + 1) * KSTEP + pos] = (uint8_t)c1;
+      for (int j = 0; j < 8; ++j) val[i][j] = 0.f;
     }
   }
+  const int pos = vtile_pos(4 * tg);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int wd = cvt_e4m3x2<false>(clamp448(val[0][j] * inv[j]), clamp448(val[1][j] * inv[j]), 0);
+    wd = cvt_e4m3x2<true>(clamp448(val[2][j] * inv[j]), clamp448(val[3][j] * inv[j]), wd);
+    *(uint32_t*)(tile + (cg * 8 + j) * VROW + pos) = nz[j] ? (uint32_t)wd : 0u;
+  }
   __syncthreads();
-  const u32x4* src = (const u32x4*)tile;
   u32x4* dst = (u32x4*)(vc + ((size_t)bh * (n_pad / KSTEP) + t) * (D * KSTEP));
-  dst[tid] = src[tid];
-  dst[tid + 256] = src[tid + 256];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ci = tid + 256 * i;
+    const int d = ci >> 2, c = ci & 3;
+    const u32x2 a = *(const u32x2*)(tile + d * VROW + c * 16);
+    const u32x2 b = *(const u32x2*)(tile + d * VROW + c * 16 + 8);
+    dst[ci] = u32x4{a[0], a[1], b[0], b[1]};
+  }
+}
+
+// All codes in one launch: grid = (q_blocks + k_blocks + n_pad/64, BH); the
+// first q_blocks blocks quantize Q (block_q tokens each), the next k_blocks
+// smoothed K (64 tokens each), the rest V (one 64-key tile each).
+template <int BQ>
+__global__ __launch_bounds__(256) void quant_fp8_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ mu, const float* __restrict__ vamax, uint8_t* __restrict__ qc,
+    float* __restrict__ qs, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
+    int N, int n_pad) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * VROW];
+  const int bh = blockIdx.y;
+  const int qb = n_pad / BQ, kb = n_pad / KSTEP;
+  const int b = blockIdx.x;
+  if (b < qb) {
+    fp8_block<BQ>(q, nullptr, qc, qs + (size_t)bh * qb, N, n_pad, bh, b, red);
+  } else if (b < qb + kb) {
+    fp8_block<KSTEP>(k, mu, kc, ks + (size_t)bh * kb, N, n_pad, bh, b - qb, red);
+  } else {
+    quant_v_tile(v, vamax, vc, N, n_pad, bh, b - qb - kb, tile);
+  }
+}
+
+// V codes alone (FP4 mode, where Q and K take the per-group kernel).
+__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
+                                                      const float* __restrict__ vamax,
+                                                      uint8_t* __restrict__ vc, int N, int n_pad) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * VROW];
+  quant_v_tile(v, vamax, vc, N, n_pad, blockIdx.y, blockIdx.x, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -266,21 +302,22 @@ void launch_quantize(const LaunchArgs& a, hipStream_t s) {
       (float*)a.stats_max);
   stats_final_kernel<<<BH, 128, 0, s>>>((const double*)a.stats_sum, (const float*)a.stats_max,
                                         a.seq_len, a.stats_splits, a.k_mean, a.v_amax, a.v_scales);
+  const int vtiles = a.n_pad / KSTEP;
   if (a.fp4) {
     quant_qk_fp4_kernel<<<dim3(a.n_pad / 32, BH, 2), 256, 0, s>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
         a.k_scales, a.seq_len, a.n_pad);
+    quant_v_kernel<<<dim3(vtiles, BH), 256, 0, s>>>((const uint16_t*)a.v, a.v_amax, a.v_codes, a.seq_len,
+                                                   a.n_pad);
   } else if (a.block_q == 128) {
-    quant_qk_fp8_kernel<128><<<dim3(a.n_pad / 128 + a.n_pad / KSTEP, BH), 256, 0, s>>>(
-        (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
-        a.k_scales, a.seq_len, a.n_pad);
+    quant_fp8_kernel<128><<<dim3(a.n_pad / 128 + a.n_pad / KSTEP + vtiles, BH), 256, 0, s>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean, a.v_amax, a.q_codes,
+        a.q_scales, a.k_codes, a.k_scales, a.v_codes, a.seq_len, a.n_pad);
   } else {
-    quant_qk_fp8_kernel<64><<<dim3(a.n_pad / 64 + a.n_pad / KSTEP, BH), 256, 0, s>>>(
-        (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
-        a.k_scales, a.seq_len, a.n_pad);
+    quant_fp8_kernel<64><<<dim3(a.n_pad / 64 + a.n_pad / KSTEP + vtiles, BH), 256, 0, s>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean, a.v_amax, a.q_codes,
+        a.q_scales, a.k_codes, a.k_scales, a.v_codes, a.seq_len, a.n_pad);
   }
-  quant_v_kernel<<<dim3(a.n_pad / KSTEP, BH), 256, 0, s>>>((const uint16_t*)a.v, a.v_amax, a.v_codes,
-                                                            a.seq_len, a.n_pad);
 }
 
 }  // namespace qsdpa
