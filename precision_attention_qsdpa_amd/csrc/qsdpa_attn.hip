@@ -24,8 +24,8 @@
 // work beside the softmax in one instruction stream.  The accumulator
 // recursion is the online-softmax one delayed by a step: step t first
 // rescales O^T by alpha(t-1), then accumulates V(t-1)^T P(t-1)^T.  Tiles are
-// 8 KB with a 16-byte-chunk XOR swizzle that keeps both the 128-bit stores and
-// the 128-bit operand reads free of bank conflicts.
+// 8 KB with a 16-byte-chunk XOR swizzle under which the 128-bit operand reads
+// show no LDS bank conflicts (SQ_LDS_BANK_CONFLICT = 0 on the Kontext shape).
 //
 // Numerics: scores are exact integer-valued FP8 dot products accumulated in
 // fp32 by the MFMA; one per-step constant c = tau*log2(e)*sQ*sK turns them
@@ -51,7 +51,7 @@ __device__ __forceinline__ int k_off(int row, int c) { return row * 128 + ((c ^ 
 // ... of an f16 K tile (256-B rows, 16 chunks).
 __device__ __forceinline__ int kh_off(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
 // ... of a V^T tile (64-B channel rows, 4 chunks).
-__device__ __forceinline__ int v_off(int d, int c) { return d * 64 + ((c ^ (((d >> 1) ^ (d >> 3)) & 3)) << 4); }
+__device__ __forceinline__ int v_off(int d, int c) { return d * 64 + ((c ^ ((d >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ v8i lds_v8i(const uint8_t* p0, const uint8_t* p1) {
   const u32x4 a = *(const u32x4*)p0, b = *(const u32x4*)p1;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     const int row = P >> 3, pc = P & 7;
     kg[i] = (uint32_t)(row * 128 + ((pc ^ ((row ^ (row >> 3)) & 7)) << 4));
     const int d = P >> 2, pv = P & 3;
-    vg[i] = (uint32_t)(d * 64 + ((pv ^ (((d >> 1) ^ (d >> 3)) & 3)) << 4));
+    vg[i] = (uint32_t)(d * 64 + ((pv ^ ((d >> 2) & 3)) << 4));
   }
   auto ring_k = [&](int t, int S) {
     const uint8_t* tp = kbase + (size_t)t * KTILE;
