@@ -158,6 +158,10 @@ __device__ __forceinline__ v8i softmax_step(v16f* s, float c, float& m, float& l
   const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
   alpha = m_new != m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
   l = alpha * l + psum;
+  // materialize l here: otherwise the compiler defers the row sums of
+  // several unrolled steps to the end of the loop body, keeping their p
+  // values live and issuing the adds as one burst with no MFMA beside them
+  asm volatile("" : "+v"(l));
   m = m_new;
   return pb;
 }
@@ -305,13 +309,18 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], wave_lds + (NSTAGE + S) * KTILE + i * 1024);
   };
 
-  auto scores = [&](const uint8_t* kbuf, v16f* s) {
+  // a00 is the operand of the first MFMA (kb = 0, h = 0), read by the caller
+  // ahead of the rescale so that its LDS latency is hidden
+  auto k_first = [&](const uint8_t* kbuf) { return lds_v8i(kbuf + koff0[0][0], kbuf + koff0[0][1]); };
+  auto scores = [&](const uint8_t* kbuf, v16f* s, const v8i& a00) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = v16f{};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const v8i a = lds_v8i(kbuf + kb * 4096 + koff0[h ^ kb][0], kbuf + kb * 4096 + koff0[h ^ kb][1]);
+        const v8i a = (kb == 0 && h == 0)
+                          ? a00
+                          : lds_v8i(kbuf + kb * 4096 + koff0[h ^ kb][0], kbuf + kb * 4096 + koff0[h ^ kb][1]);
         s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb8[h], s[kb], 0, 0, 0, 127, 0, 127);
       }
     }
@@ -321,8 +330,12 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   for (int i = 0; i < 4; ++i) o[i] = v16f{};
   float m = -INFINITY, l = 0.f;
 
+  // K-block scale of the step whose softmax runs next.  Each step loads the
+  // next one just before its barrier wait, which covers the scalar load; a
+  // load next to the LDS reads would make their waits include it.
+  float kscn = ksc[0];
   auto softmax = [&](int t, v16f* s, auto full_t, float& alpha) -> v8i {
-    return softmax_step<decltype(full_t)::value>(s, cscale * ksc[t], m, l, alpha, t * KSTEP, N, g);
+    return softmax_step<decltype(full_t)::value>(s, cscale * kscn, m, l, alpha, t * KSTEP, N, g);
   };
   auto rescale = [&](float alpha) { rescale_o(o, alpha); };
   auto pv = [&](const v8i& pb, const uint8_t* vbuf) { value_mfma(o, pb, vbuf, voff0, voff1); };
@@ -344,24 +357,30 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   __builtin_amdgcn_s_waitcnt(0x0070 | 8);
   asm volatile("s_barrier" ::: "memory");
   v16f sa[2], sb[2];
-  scores(lds_k(0), sa);
+  scores(lds_k(0), sa, k_first(lds_k(0)));
   v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;
 
   // steps 0 .. T-2 (full)
+  // Instruction order of a step: the 8 MFMAs (4 scores, 4 values) spread
+  // over the ~170 VALU instructions of the softmax, 22 after each, and the
+  // two LDS reads of each MFMA operand issued right after the MFMA before it.
   auto step = [&](int t, v16f* s_cur, v16f* s_next, auto st) {
     constexpr int S = decltype(st)::value;   // t % 4
+    const v8i a00 = k_first(lds_k((S + 1) & 3));
     rescale(alpha_prev);
     ring_k(min(t + 4, Tm1), S);
     ring_v(min(t + 2, Tm1), (S + 2) & 3);
-    scores(lds_k((S + 1) & 3), s_next);
+    scores(lds_k((S + 1) & 3), s_next, a00);
     pv(pb_prev, lds_v((S + 3) & 3));
     pb_prev = softmax(t, s_cur, std::true_type{}, alpha_prev);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+      if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x402, 22, 0);         // VALU
     }
+    kscn = ksc[t + 1];
     ring_barrier_wait8();
   };
   int t = 0;
@@ -375,12 +394,14 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   // the ring stage is t & 3 computed at run time), then the last step T-1
   auto step_dyn = [&](int tt, v16f* s_cur, v16f* s_next) {
     const int S = tt & 3;
+    const v8i a00 = k_first(lds_k((S + 1) & 3));
     rescale(alpha_prev);
     ring_k(min(tt + 4, Tm1), S);
     ring_v(min(tt + 2, Tm1), (S + 2) & 3);
-    scores(lds_k((S + 1) & 3), s_next);
+    scores(lds_k((S + 1) & 3), s_next, a00);
     pv(pb_prev, lds_v((S + 3) & 3));
     pb_prev = softmax(tt, s_cur, std::true_type{}, alpha_prev);
+    kscn = ksc[tt + 1];
     ring_barrier_wait8();
   };
   auto last = [&](int tl, v16f* s_cur) {
