@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define QSDPA_ABI_VERSION 1
+#define QSDPA_ABI_VERSION 2
 #define QSDPA_HEAD_DIM 128
 
 /* Status codes (return values). */
@@ -97,9 +97,16 @@ typedef struct qsdpa_params {
  *   v_scales:         fp32 [BH][128] (sV).
  *   v_amax:           fp32 [BH][128] (vmax).
  *   stats:            scratch for partial channel sums (fp64) and maxima.
+ *   k_expanded:       FP4 mode only (0 bytes in FP8 mode): every K element
+ *                     x = code * scale split into f16 hi = f16(x) and
+ *                     lo = f16(x - hi), both rounded to nearest even, as
+ *                     f16 [BH][n_pad/64][2][64][128]: per 64-key tile the
+ *                     hi tile, then the lo tile; in a key row the 8-channel
+ *                     chunk c is stored at chunk position c ^ (key & 15).
  */
 typedef struct qsdpa_layout {
   uint64_t q_codes, q_scales, k_codes, k_scales, k_mean, v_codes, v_scales, v_amax, stats;
+  uint64_t k_expanded;
   uint64_t total;          /* bytes needed (= qsdpa_workspace_bytes) */
   int32_t n_pad;
   int32_t code_row_bytes;  /* 128 (FP8) or 64 (FP4) */
@@ -127,6 +134,7 @@ int qsdpa_workspace_layout(const qsdpa_params* p, qsdpa_layout* out);
 /*
  * Steps 1-4: channel statistics, K smoothing and the Q/K/V codes and scales,
  * written into the workspace (layout above).  q, k, v: bf16 [B,H,N,128].
+ * In FP4 mode it also writes k_expanded from the K codes and scales.
  */
 int qsdpa_quantize(const qsdpa_params* p, const void* q, const void* k, const void* v,
                    void* workspace, size_t ws_bytes, void* stream);

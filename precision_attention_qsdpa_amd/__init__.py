@@ -37,9 +37,13 @@ class QsdpaParams(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
+ABI_VERSION = 2   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
+
+
 class QsdpaLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("q_codes", "q_scales", "k_codes", "k_scales", "k_mean",
-                                               "v_codes", "v_scales", "v_amax", "stats", "total")] + \
+                                               "v_codes", "v_scales", "v_amax", "stats", "k_expanded",
+                                               "total")] + \
                [(n, ctypes.c_int32) for n in ("n_pad", "code_row_bytes", "q_scale_count", "k_scale_count",
                                               "stats_splits")] + [("reserved", ctypes.c_int32 * 3)]
 
@@ -79,6 +83,9 @@ def load() -> ctypes.CDLL:
     lib.qsdpa_attention.argtypes = [P, vp, sz, vp, vp]
     lib.qsdpa_forward.restype = ctypes.c_int
     lib.qsdpa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    if lib.qsdpa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.qsdpa_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild it with `python -m precision_attention_qsdpa_amd.build`")
     _LIB = lib
     return lib
 

@@ -24,6 +24,9 @@ FLAGS = [
     # keep the next step's score MFMAs in the block where they are written, so
     # they interleave with the softmax instead of sinking past its branch
     "-mllvm", "-disable-machine-sink",
+    # MFMA results and accumulators in VGPRs: the softmax and the rescale work
+    # on them with VALU instructions, which cannot read AGPRs without copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

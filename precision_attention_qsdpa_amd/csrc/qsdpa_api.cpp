@@ -61,6 +61,7 @@ void make_layout(const qsdpa_params* p, qsdpa_layout* L) {
   L->v_scales = take(bh * QSDPA_HEAD_DIM * 4);
   L->v_amax = take(bh * QSDPA_HEAD_DIM * 4);
   L->stats = take(bh * L->stats_splits * QSDPA_HEAD_DIM * (8 + 4));
+  L->k_expanded = take(fp4 ? bh * n_pad * QSDPA_HEAD_DIM * 4 : 0);
   L->total = off;
 }
 
@@ -97,6 +98,7 @@ qsdpa::LaunchArgs make_args(const qsdpa_params* p, const qsdpa_layout& L, const 
   a.v_codes = w + L.v_codes;
   a.v_scales = (float*)(w + L.v_scales);
   a.v_amax = (float*)(w + L.v_amax);
+  a.k_expanded = w + L.k_expanded;
   a.stats_sum = w + L.stats;
   a.stats_max = w + L.stats + (uint64_t)p->batch * p->heads * L.stats_splits * QSDPA_HEAD_DIM * 8;
   return a;

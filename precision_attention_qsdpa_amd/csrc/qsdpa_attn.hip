@@ -39,8 +39,6 @@
 
 namespace qsdpa {
 
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-
 constexpr int WAVES = 4;
 constexpr int QW = 32;              // queries per wave
 constexpr int QT = QW * WAVES;      // queries per workgroup
@@ -48,8 +46,6 @@ constexpr int KTILE = KSTEP * D;    // bytes of an FP8 K tile / V^T tile
 
 // LDS byte offset of 16-byte chunk c of row `row` in an FP8 K tile (128-B rows).
 __device__ __forceinline__ int k_off(int row, int c) { return row * 128 + ((c ^ ((row ^ (row >> 3)) & 7)) << 4); }
-// ... of an f16 K tile (256-B rows, 16 chunks).
-__device__ __forceinline__ int kh_off(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
 // ... of a V^T tile (64-B channel rows, 4 chunks).
 __device__ __forceinline__ int v_off(int d, int c) { return d * 64 + ((c ^ ((d >> 2) & 3)) << 4); }
 
@@ -78,12 +74,6 @@ __device__ __forceinline__ int undef_int() {
   int x;
   asm volatile("" : "=v"(x));
   return x;
-}
-
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const float mag = e ? (float)((2u + m) << (e - 1u)) * 0.5f : (float)m * 0.5f;
-  return (c & 8u) ? -mag : mag;
 }
 
 // Maps the hardware workgroup id so that each XCD (ids are dealt round-robin
@@ -434,21 +424,36 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
 
 // ---------------------------------------------------------------------------
 // FP4 kernel: Q and K arrive as E2M1 codes with an fp32 scale per 16
-// channels.  Q is dequantized once into registers and each K tile once per
-// workgroup into LDS, both as f16 pairs hi = f16(x), lo = f16(x - hi), which
-// carry x to about 2^-22 relative; the scores are three f16 MFMAs per
-// 16-channel chunk (hi.hi + lo.hi + hi.lo), so they keep fp32-level accuracy
-// while P and V stay FP8.  Tiles are staged through registers (the K tile is
-// expanded 4x on the way); during step t the LDS holds K(t+1) and V(t-1)
-// and the registers bring in K(t+2) and V(t) (two buffers each, one barrier
-// per step).  One wave per SIMD: the f16 operands need more registers.
+// channels.  Q is dequantized once into registers, and K comes as the f16
+// hi/lo tiles the quantize pass expanded (hi = f16(x), lo = f16(x - hi),
+// about 2^-22 relative), so the scores are three f16 MFMAs per 16-channel
+// chunk (hi.hi + lo.hi + hi.lo) and keep fp32-level accuracy while P and V
+// stay FP8.  The tiles reach LDS as in the FP8 kernel, by asynchronous copies
+// (global_load_lds_dwordx4), through a ring of 3 stages of 32 KB K + 8 KB V^T
+// issued 2 steps before they are read:
+//   step t reads K(t+1) and V(t-1), and issues K(t+3) and V(t+1);
+// each wave issues 10 copies per step, so at the end of step t it waits until
+// at most 10 are outstanding (those of step t): K(t+2) and V(t) have landed.
+// One wave per SIMD: the f16 Q operand alone takes 64 registers.
 // ---------------------------------------------------------------------------
+constexpr int NSTAGE4 = 3;
+
+__device__ __forceinline__ void ring_barrier_wait10() {
+  // s_waitcnt vmcnt(10) lgkmcnt(0), then the barrier
+  __builtin_amdgcn_s_waitcnt(0x0070 | 10);
+  asm volatile("s_barrier" ::: "memory");
+}
+
 __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
-    const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kc,
-    const float* __restrict__ ks, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
-    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][4 * KTILE];   // hi tile, then lo tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][KTILE];
+    const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kx,
+    const uint8_t* __restrict__ vc, const float* __restrict__ vs, uint16_t* __restrict__ out, int N,
+    int n_pad, float tau_log2e, int tiles_per_bh) {
+  // ring: stages 0..2 of expanded K tiles (hi then lo), then stages 0..2 of V^T tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE4 * (KXTILE + KTILE)];
+  auto lds_k = [&](int S) -> uint8_t* { return ring + S * KXTILE; };
+  auto lds_v = [&](int S) -> uint8_t* { return ring + NSTAGE4 * KXTILE + S * KTILE; };
+  const uint32_t ring_lds = lds_addr(ring);
+  const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / tiles_per_bh, tile = wg - bh * tiles_per_bh;
@@ -472,64 +477,44 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
       }
     }
   }
-  const uint8_t* kbase = kc + (size_t)bh * n_pad * 64;
-  const float* ksc = ks + (size_t)bh * n_pad * 8;
+  const uint8_t* kxbase = kx + (size_t)bh * (n_pad / KSTEP) * KXTILE;
   const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
   const int voff0 = v_off(r, 2 * g), voff1 = v_off(r, 2 * g + 1);
-  const int vst0 = v_off(tid >> 2, tid & 3), vst1 = v_off((tid + 256) >> 2, tid & 3);
 
-  // staging: this thread handles (key, 16-channel group) pairs tid and tid + 256
-  uint32_t kcode[2][2];
-  float kscl[2];
-  u32x4 vreg[2];
-  auto load_k = [&](int t) {
+  // Ring copies.  An expanded K tile is already in LDS order: wave w copies
+  // its 1 KB pieces 8w .. 8w+7 unchanged.  V^T tiles as in the FP8 kernel:
+  // wave w's instruction i fills LDS chunks (2w+i)*64 + lane of a stage with
+  // the global chunk the swizzle puts there.
+  const uint32_t kgl = (uint32_t)lane * 16u;
+  uint32_t vg[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci >> 3, grp = ci & 7;
-      const u32x2 w = *(const u32x2*)(kbase + ((size_t)t * KSTEP + key) * 64 + grp * 8);
-      kcode[i][0] = w[0];
-      kcode[i][1] = w[1];
-      kscl[i] = ksc[((size_t)t * KSTEP + key) * 8 + grp];
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int P = (2 * wave + i) * 64 + lane;
+    const int d = P >> 2, pv = P & 3;
+    vg[i] = (uint32_t)(d * 64 + ((pv ^ ((d >> 2) & 3)) << 4));
+  }
+  auto ring_k = [&](int t, int S) {
+    const uint8_t* tp = kxbase + (size_t)t * KXTILE + wave_u * 8192u;
+    const uint32_t dst = ring_lds + (uint32_t)S * KXTILE + wave_u * 8192u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ring_copy16(tp + i * 1024, kgl, dst + i * 1024);
   };
-  auto load_v = [&](int t) {
+  auto ring_v = [&](int t, int S) {
     const uint8_t* tp = vbase + (size_t)t * KTILE;
-    vreg[0] = *(const u32x4*)(tp + tid * 16);
-    vreg[1] = *(const u32x4*)(tp + tid * 16 + 4096);
-  };
-  auto store_k = [&](uint8_t* kbuf) {
+    const uint32_t dst = ring_lds + NSTAGE4 * KXTILE + (uint32_t)S * KTILE + wave_u * 2048u;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci >> 3, grp = ci & 7;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        v8h hv, lv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = e2m1_value((kcode[i][half] >> (4 * e)) & 15u) * kscl[i];
-          hv[e] = (_Float16)x;
-          lv[e] = (_Float16)(x - (float)hv[e]);
-        }
-        *(v8h*)(kbuf + kh_off(key, 2 * grp + half)) = hv;
-        *(v8h*)(kbuf + 2 * KTILE + kh_off(key, 2 * grp + half)) = lv;
-      }
-    }
+    for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], dst + i * 1024);
   };
-  auto store_v = [&](uint8_t* vbuf) {
-    *(u32x4*)(vbuf + vst0) = vreg[0];
-    *(u32x4*)(vbuf + vst1) = vreg[1];
-  };
+
+  // scores of a 64-key tile (keys 0..31, then 32..63)
   auto scores = [&](const uint8_t* kbuf, v16f* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = v16f{};
-      const int row = kb * 32 + r;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const v8h ah = *(const v8h*)(kbuf + kh_off(row, 2 * c + g));
-        const v8h al = *(const v8h*)(kbuf + 2 * KTILE + kh_off(row, 2 * c + g));
+        const v8h ah = *(const v8h*)(kbuf + kh_off(kb * 32 + r, 2 * c + g));
+        const v8h al = *(const v8h*)(kbuf + KXTILE / 2 + kh_off(kb * 32 + r, 2 * c + g));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qhi[c], s[kb], 0, 0, 0);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qhi[c], s[kb], 0, 0, 0);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qlo[c], s[kb], 0, 0, 0);
@@ -542,60 +527,66 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
   for (int i = 0; i < 4; ++i) o[i] = v16f{};
   float m = -INFINITY, l = 0.f;
 
-  // prologue: K(0), K(1) in LDS; V buffer 1 (read by the zero-weight value
-  // product of step -1) cleared
-  load_k(0);
-  store_k(lds_k[0]);
-  if (T > 1) {
-    load_k(1);
-    store_k(lds_k[1]);
-  }
-  *(u32x4*)(lds_v[1] + vst0) = u32x4{0u, 0u, 0u, 0u};
-  *(u32x4*)(lds_v[1] + vst1) = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  // prologue: K(0..2) and V(0) in flight; V(-1) (stage 2) is zero.  The Q
+  // operand loads complete first, so that from here on the only vector-memory
+  // loads in flight are ring copies.
+  const int Tm1 = T - 1;
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+  ring_k(0, 0);
+  ring_k(min(1, Tm1), 1);
+  ring_k(min(2, Tm1), 2);
+  ring_v(0, 0);
+  *(u32x4*)(lds_v(2) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+  *(u32x4*)(lds_v(2) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
+  // K(0), K(1) landed (at most K(2) and V(0) outstanding)
+  ring_barrier_wait10();
   v16f sa[2], sb[2];
-  scores(lds_k[0], sa);
+  scores(lds_k(0), sa);
   v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;
 
-  // steps 0 .. T-2 (full)
-  auto step = [&](int t, v16f* s_cur, v16f* s_next, auto par) {
-    constexpr int P = decltype(par)::value;   // t & 1
+  // steps 0 .. T-2 (full); S = t % 3 is the stage of K(t) and V(t)
+  auto step = [&](int t, int S, v16f* s_cur, v16f* s_next) {
+    const int S1 = S == 2 ? 0 : S + 1, S2 = S == 0 ? 2 : S - 1;
     rescale_o(o, alpha_prev);
-    load_k(min(t + 2, T - 1));
-    load_v(t);
-    scores(lds_k[P ^ 1], s_next);
-    value_mfma(o, pb_prev, lds_v[P ^ 1], voff0, voff1);
+    ring_k(min(t + 3, Tm1), S);
+    ring_v(min(t + 1, Tm1), S1);
+    scores(lds_k(S1), s_next);
+    value_mfma(o, pb_prev, lds_v(S2), voff0, voff1);
     pb_prev = softmax_step<true>(s_cur, tau_log2e, m, l, alpha_prev, t * KSTEP, N, g);
-    store_k(lds_k[P]);
-    store_v(lds_v[P]);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 52; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);   // VALU
+    }
+    ring_barrier_wait10();
   };
-  int t = 0;
+  int t = 0, S = 0;
   for (; t + 2 < T; t += 2) {
-    step(t, sa, sb, std::integral_constant<int, 0>{});
-    step(t + 1, sb, sa, std::integral_constant<int, 1>{});
+    step(t, S, sa, sb);
+    S = S == 2 ? 0 : S + 1;
+    step(t + 1, S, sb, sa);
+    S = S == 2 ? 0 : S + 1;
   }
-  // the last step T-1 (possibly short)
-  auto last = [&](int tl, v16f* s_cur, auto par) {
-    constexpr int P = decltype(par)::value;
+  // the last step T-1 (possibly short); V(T-1) is in stage (T-1) % 3
+  auto last = [&](int tl, int St, v16f* s_cur) {
+    const int S2 = St == 0 ? 2 : St - 1;
     rescale_o(o, alpha_prev);
-    load_v(tl);
-    value_mfma(o, pb_prev, lds_v[P ^ 1], voff0, voff1);
+    value_mfma(o, pb_prev, lds_v(S2), voff0, voff1);
     float alpha;
     const v8i pb = (tl + 1) * KSTEP <= N
                        ? softmax_step<true>(s_cur, tau_log2e, m, l, alpha, tl * KSTEP, N, g)
                        : softmax_step<false>(s_cur, tau_log2e, m, l, alpha, tl * KSTEP, N, g);
-    store_v(lds_v[P]);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0070);   // every ring copy has landed
+    asm volatile("s_barrier" ::: "memory");
     rescale_o(o, alpha);
-    value_mfma(o, pb, lds_v[P], voff0, voff1);
+    value_mfma(o, pb, lds_v(St), voff0, voff1);
   };
   if (t + 1 < T) {
-    step(t, sa, sb, std::integral_constant<int, 0>{});
-    last(t + 1, sb, std::integral_constant<int, 1>{});
+    step(t, S, sa, sb);
+    last(t + 1, S == 2 ? 0 : S + 1, sb);
   } else {
-    last(t, sa, std::integral_constant<int, 0>{});
+    last(t, S, sa);
   }
 
   const int q = q0 + r;
@@ -607,8 +598,8 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
   const int tiles = a.n_pad / QT;
   const float tl = a.softmax_scale * LOG2E;
   if (a.fp4) {
-    attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes,
-                                                a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles);
+    attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded, a.v_codes, a.v_scales,
+                                                (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles);
   } else {
     attn_fp8_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes,
                                                 a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,

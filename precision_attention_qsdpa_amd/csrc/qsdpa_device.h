@@ -9,6 +9,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int D = 128;          // head dimension
 constexpr int KSTEP = 64;       // keys per online-softmax step (also the K scale block)
@@ -49,6 +50,20 @@ __device__ __forceinline__ uint32_t e2m1_code(float x) {
                (y >= 3.5f) + (y > 5.0f);
   return c | ((__float_as_uint(x) >> 28) & 8u);
 }
+
+// Value of an E2M1 code (sign bit 3, exponent bits 2..1, mantissa bit 0).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float mag = e ? (float)((2u + m) << (e - 1u)) * 0.5f : (float)m * 0.5f;
+  return (c & 8u) ? -mag : mag;
+}
+
+// Bytes of one 64-key tile of FP4-mode K expanded to f16 hi + lo (2 x 16 KB),
+// and the byte offset of 8-channel chunk c of key row `row` inside the hi (or
+// lo) half: rows of 256 B, chunk c stored at position c ^ (row & 15), so the
+// 16 lanes that read one chunk column of 16 rows hit 16 different positions.
+constexpr int KXTILE = 2 * KSTEP * D * 2;
+__device__ __forceinline__ int kh_off(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

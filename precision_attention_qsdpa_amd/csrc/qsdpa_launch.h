@@ -27,6 +27,7 @@ struct LaunchArgs {
   uint8_t* v_codes;
   float* v_scales;
   float* v_amax;
+  uint8_t* k_expanded;   // FP4 mode: K as f16 hi/lo tiles
   void* stats_sum;
   void* stats_max;
 };

@@ -59,6 +59,15 @@ def read_workspace(ws: torch.Tensor, params, N: int) -> dict:
     out["v_codes_pad"] = nat[:, :, N:]
     out["q_codes_pad"] = sec(L.q_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, N:]
     out["k_codes_pad"] = sec(L.k_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, N:]
+    if params.qk_format == qs.QSDPA_QK_FP4_E2M1:
+        # expanded K: per 64-key tile hi then lo, 8-channel chunk c of key row r at position c ^ (r & 15)
+        x = sec(L.k_expanded, BH * L.n_pad * 256, np.uint16).reshape(B, H, L.n_pad // 64, 2, 64, 16, 8)
+        r = np.arange(64)[:, None]
+        pos = np.arange(16)[None, :] ^ (r & 15)                  # [64 rows, 16 chunks] -> stored position
+        nat = np.take_along_axis(x, pos[None, None, None, None, :, :, None], axis=5)
+        nat = nat.reshape(B, H, L.n_pad // 64, 2, 64, 128).transpose(0, 1, 3, 2, 4, 5).reshape(B, H, 2, L.n_pad, 128)
+        out["k_hi"], out["k_lo"] = nat[:, :, 0, :N], nat[:, :, 1, :N]
+        out["k_hilo_pad"] = nat[:, :, :, N:]
     return out
 
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert qs.load().qsdpa_abi_version() == 1
+    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 2
     for st in range(-6, 1):
         assert qs.status_string(st) not in ("", "unknown status")
     assert qs.status_string(-99) == "unknown status"
@@ -73,7 +73,8 @@ def _round(x, a):
                                           (1, 1, 1000, "fp4", 64)])
 def test_workspace_closed_form(B, H, N, fmt, bq):
     """One byte per Q/K code in FP8 mode (half a byte in FP4 mode), one byte per
-    V code, fp32 scales, padded to 128 tokens, 256-byte aligned sections."""
+    V code, fp32 scales, padded to 128 tokens, 256-byte aligned sections; in
+    FP4 mode also the f16 hi/lo expansion of K (4 bytes per element)."""
     p = qs.make_params(B, H, N, fmt=fmt, block_q=bq)
     L = qs.qsdpa_workspace_layout(p)
     BH, npad = B * H, _round(N, 128)
@@ -82,16 +83,19 @@ def test_workspace_closed_form(B, H, N, fmt, bq):
     qsc = npad // bq if fmt == "fp8" else npad * 8
     ksc = npad // 64 if fmt == "fp8" else npad * 8
     sizes = [BH * npad * crb, BH * npad * crb, BH * npad * 128, BH * qsc * 4, BH * ksc * 4,
-             BH * 512, BH * 512, BH * 512, BH * splits * 128 * 12]
+             BH * 512, BH * 512, BH * 512, BH * splits * 128 * 12,
+             BH * npad * 128 * 4 if fmt == "fp4" else 0]
     assert (L.n_pad, L.code_row_bytes, L.q_scale_count, L.k_scale_count, L.stats_splits) == (npad, crb, qsc, ksc, splits)
     assert L.total == sum(_round(s, 256) for s in sizes)
     assert qs.qsdpa_workspace_bytes(p) == L.total
-    offs = [L.q_codes, L.k_codes, L.v_codes, L.q_scales, L.k_scales, L.k_mean, L.v_scales, L.v_amax, L.stats]
+    offs = [L.q_codes, L.k_codes, L.v_codes, L.q_scales, L.k_scales, L.k_mean, L.v_scales, L.v_amax, L.stats,
+            L.k_expanded]
     for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [L.total]):
         assert o % 256 == 0 and o + s <= o2
     # FP8 halves the bf16 bytes of Q, K and V; FP4 Q/K codes (V stays FP8) cut them 3x
     qkv_bf16 = 3 * BH * N * 128 * 2
     codes = sizes[0] + sizes[1] + sizes[2]
+    assert (L.k_expanded == L.total) == (fmt == "fp8")
     if N % 128 == 0:
         assert codes * (2 if fmt == "fp8" else 3) == qkv_bf16
 

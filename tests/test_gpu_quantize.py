@@ -39,7 +39,18 @@ def check_quantize(qb, kb, vb, fmt, block_q, heads, label):
             if not ok:
                 bad = np.argwhere(g.reshape(want.shape) != want)
                 pytest.fail(f"{label} {name} (b={b},h={h}): {len(bad)} mismatches, first at {bad[:3].tolist()}")
-    for name in ("q_codes_pad", "k_codes_pad", "v_codes_pad", "q_scales_pad", "k_scales_pad"):
+        if fmt == "fp4":
+            # the f16 pair the FP4 score MFMAs take: hi = f16(x), lo = f16(x - hi) in fp32,
+            # x = fp32 of the oracle's exact code * scale
+            x = oracle.dequantize_qk(z.k_codes, z.k_scales, fmt, 16, 0, 0).astype(np.float32)
+            hi = x.astype(np.float16)
+            lo = (x - hi.astype(np.float32)).astype(np.float16)
+            for name, want in (("k_hi", hi), ("k_lo", lo)):
+                g = got[name][b, h]
+                if not np.array_equal(g, want.view(np.uint16)):
+                    bad = np.argwhere(g != want.view(np.uint16))
+                    pytest.fail(f"{label} {name} (b={b},h={h}): {len(bad)} mismatches, first at {bad[:3].tolist()}")
+    for name in ("q_codes_pad", "k_codes_pad", "v_codes_pad", "q_scales_pad", "k_scales_pad", "k_hilo_pad"):
         if name in got:
             assert not np.any(got[name]), f"{label}: {name} not zero"
 
