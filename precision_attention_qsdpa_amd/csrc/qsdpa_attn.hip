@@ -506,19 +506,24 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
     for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], dst + i * 1024);
   };
 
-  // scores of a 64-key tile (keys 0..31, then 32..63)
+  // scores of a 64-key tile: the chains of keys 0..31 and 32..63 interleaved
   auto scores = [&](const uint8_t* kbuf, v16f* s) {
+    s[0] = v16f{};
+    s[1] = v16f{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = v16f{};
+    for (int c = 0; c < 8; ++c) {
+      v8h ah[2], al[2];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const v8h ah = *(const v8h*)(kbuf + kh_off(kb * 32 + r, 2 * c + g));
-        const v8h al = *(const v8h*)(kbuf + KXTILE / 2 + kh_off(kb * 32 + r, 2 * c + g));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qhi[c], s[kb], 0, 0, 0);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qhi[c], s[kb], 0, 0, 0);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qlo[c], s[kb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) {
+        ah[kb] = *(const v8h*)(kbuf + kh_off(kb * 32 + r, 2 * c + g));
+        al[kb] = *(const v8h*)(kbuf + KXTILE / 2 + kh_off(kb * 32 + r, 2 * c + g));
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[kb], qhi[c], s[kb], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[kb], qhi[c], s[kb], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[kb], qlo[c], s[kb], 0, 0, 0);
     }
   };
 
