@@ -48,6 +48,19 @@ head dimension D = 128, queries i and keys j:
 
 The step of 64 keys matters: P's codes are taken relative to the running
 maximum, so a different step gives different codes.
+
+MXFP4 mode (beyond the pages)
+-----------------------------
+The pages' FP4 scheme has an fp32 scale per 16 channels.  The MXFP4 mode
+instead follows the OCP Microscaling Formats (MX) specification v1.0 (the
+FP4 E2M1 element type with a shared E8M0 scale per block of 32 elements),
+the block format that the scaled MFMA of the target GPU applies in hardware.
+Step 3 becomes, for each token and each block of 32 consecutive channels
+with a = max |x|: if a == 0 the scale byte and all codes are 0; otherwise
+the shared exponent is floor(log2 a) minus 2 (the exponent of E2M1's largest
+normal value 6 = 1.5 * 2**2), stored biased by 127 and clamped to [0, 254];
+X = 2**(byte - 127) and code = E2M1(x / X), nearest even, saturating at 6
+(so magnitudes in (6 X, 8 X) become 6 X).  Steps 1, 2 and 4-7 are unchanged.
 """
 from __future__ import annotations
 
@@ -60,6 +73,9 @@ from .formats import E2M1, E4M3, bf16_bits_to_f64, decode, encode, f32, f64_to_b
 
 FP8 = "fp8"
 FP4 = "fp4"
+MXFP4 = "mxfp4"
+MX_BLOCK = 32          # channels per E8M0 scale in MXFP4 mode
+E8M0_BIAS = 127
 P_SCALE = 448.0        # P codes are E4M3(448 p): p <= 1 fills the FP8 range
 SOFTMAX_STEP = 64      # keys per online-softmax step
 FP4_GROUP = 16         # channels per FP4 scale
@@ -128,6 +144,26 @@ def quantize_fp4_groups(x32: np.ndarray, group: int = FP4_GROUP):
     return packed, scales
 
 
+def quantize_mxfp4_blocks(x32: np.ndarray, block: int = MX_BLOCK):
+    """MXFP4 codes: per (token, 32-channel block) a shared power-of-two scale.
+    x32 float32 [B,H,N,D] -> (packed uint8 [B,H,N,D/2], scale bytes uint8
+    [B,H,N,D/32]).  The scale byte is the biased exponent e of X = 2**(e-127);
+    codes as in FP4 mode (two per byte, the even channel in the low nibble)."""
+    B, H, N, D = x32.shape
+    g = x32.astype(np.float64).reshape(B, H, N, D // block, block)
+    amax = np.abs(g).max(axis=4)
+    _, e = np.frexp(amax)                      # amax = f * 2**e, f in [0.5, 1)
+    shared = (e - 1) - 2                       # floor(log2 amax) - emax(E2M1)
+    byte = np.clip(shared + E8M0_BIAS, 0, 254)
+    byte = np.where(amax > 0, byte, 0).astype(np.uint8)
+    X = np.ldexp(1.0, byte.astype(np.int64) - E8M0_BIAS)
+    vals = round_to(g / X[..., None], E2M1)    # x / X is exact: X is a power of two
+    vals = np.where(amax[..., None] > 0, vals, 0.0)
+    codes = encode(vals, E2M1).reshape(B, H, N, D)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, byte
+
+
 def unpack_fp4(packed: np.ndarray) -> np.ndarray:
     """Inverse of the nibble packing: uint8 [..., D/2] -> codes [..., D]."""
     out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
@@ -151,8 +187,8 @@ class Quantized:
     fmt: str
     block_q: int
     block_k: int
-    q_codes: np.ndarray   # fp8: uint8 [B,H,N,D]; fp4: packed uint8 [B,H,N,D/2]
-    q_scales: np.ndarray  # fp8: fp32 [B,H,nQ];   fp4: fp32 [B,H,N,D/16]
+    q_codes: np.ndarray   # fp8: uint8 [B,H,N,D]; fp4, mxfp4: packed uint8 [B,H,N,D/2]
+    q_scales: np.ndarray  # fp8: fp32 [B,H,nQ];   fp4: fp32 [B,H,N,D/16]; mxfp4: E8M0 bytes [B,H,N,D/32]
     k_codes: np.ndarray
     k_scales: np.ndarray
     k_mean: np.ndarray    # fp32 [B,H,D]
@@ -163,7 +199,7 @@ class Quantized:
 
 def quantize(q_bits, k_bits, v_bits, *, fmt: str = FP8, block_q: int = 128, block_k: int = 64) -> Quantized:
     """Steps 1-4 for bf16 bit patterns (uint16 [B,H,N,D])."""
-    if fmt not in (FP8, FP4):
+    if fmt not in (FP8, FP4, MXFP4):
         raise ValueError(fmt)
     q = bf16_bits_to_f64(q_bits)
     k = bf16_bits_to_f64(k_bits)
@@ -174,9 +210,12 @@ def quantize(q_bits, k_bits, v_bits, *, fmt: str = FP8, block_q: int = 128, bloc
     if fmt == FP8:
         qc, qs = quantize_fp8_blocks(q32, block_q)
         kc, kscl = quantize_fp8_blocks(ks, block_k)
-    else:
+    elif fmt == FP4:
         qc, qs = quantize_fp4_groups(q32)
         kc, kscl = quantize_fp4_groups(ks)
+    else:
+        qc, qs = quantize_mxfp4_blocks(q32)
+        kc, kscl = quantize_mxfp4_blocks(ks)
     vc, vs = quantize_v(v, vmax)
     return Quantized(fmt, block_q, block_k, qc, qs, kc, kscl, mu, vc, vs, vmax)
 
@@ -190,6 +229,9 @@ def dequantize_qk(codes, scales, fmt: str, block: int, b: int, h: int) -> np.nda
         return vals * s[:, None]
     vals = decode(unpack_fp4(codes[b, h]), E2M1)
     N, D = vals.shape
+    if fmt == MXFP4:
+        s = np.ldexp(1.0, scales[b, h].astype(np.int64) - E8M0_BIAS)   # [N, D/32]
+        return (vals.reshape(N, D // MX_BLOCK, MX_BLOCK) * s[:, :, None]).reshape(N, D)
     s = scales[b, h].astype(np.float64)                     # [N, D/16]
     return (vals.reshape(N, D // FP4_GROUP, FP4_GROUP) * s[:, :, None]).reshape(N, D)
 

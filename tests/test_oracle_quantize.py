@@ -119,7 +119,7 @@ def test_k_smoothing_removes_constant_key_offset_exactly():
     z2 = oracle.quantize(_bits(q), _bits(k + c), _bits(v), block_q=64, block_k=64)
     assert np.array_equal(z2.k_mean, z1.k_mean + c)
     assert np.array_equal(z1.k_codes, z2.k_codes) and np.array_equal(z1.k_scales, z2.k_scales)
-    for fmt in ("fp4",):
+    for fmt in ("fp4", "mxfp4"):
         a = oracle.quantize(_bits(q), _bits(k), _bits(v), fmt=fmt)
         b = oracle.quantize(_bits(q), _bits(k + c), _bits(v), fmt=fmt)
         assert np.array_equal(a.k_codes, b.k_codes) and np.array_equal(a.k_scales, b.k_scales)
