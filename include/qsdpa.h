@@ -62,9 +62,16 @@ extern "C" {
 #define QSDPA_ERR_ALIAS (-5)               /* O overlaps an input or the workspace */
 #define QSDPA_ERR_HIP (-6)                 /* a kernel launch failed */
 
-/* Q/K precision.  P and V are FP8 E4M3 in both. */
+/* Q/K precision.  P and V are FP8 E4M3 in every mode.
+ * MXFP4 (beyond the pages' FP4): E2M1 codes with one shared E8M0 (power of
+ * two) scale per 32 consecutive channels, as in the OCP Microscaling Formats
+ * specification v1.0; the shared exponent is floor(log2 amax) - 2, biased by
+ * 127 and clamped to [0, 254] (0 for an all-zero block), and the codes are
+ * E2M1(x / 2**(byte - 127)), nearest even, saturating at 6.  block_q, block_k
+ * and fp4_group are ignored in this mode. */
 #define QSDPA_QK_FP8_E4M3 0
 #define QSDPA_QK_FP4_E2M1 1
+#define QSDPA_QK_MXFP4_E2M1 2
 
 typedef struct qsdpa_params {
   int32_t batch;         /* B >= 1 */
@@ -83,12 +90,18 @@ typedef struct qsdpa_params {
  * N is padded to n_pad = round_up(N, 128); padded tokens hold zero codes.
  * BH = B*H, (b,h) index bh = b*H + h.
  *   q_codes, k_codes: uint8 [BH][n_pad][code_row_bytes]; FP8: one E4M3 code
- *                     per channel; FP4: two E2M1 codes per byte, the even
- *                     channel in the low nibble.
+ *                     per channel; FP4, MXFP4: two E2M1 codes per byte, the
+ *                     even channel in the low nibble.
  *   q_scales:         fp32 [BH][q_scale_count]; FP8: per block_q tokens
  *                     (q_scale_count = n_pad/block_q, blocks past N are 0);
  *                     FP4: [BH][n_pad][8], one per 16 channels.
- *   k_scales:         as q_scales with block_k.
+ *                     MXFP4: uint8 E8M0 bytes [BH][n_pad][4], one per 32
+ *                     channels (q_scale_count = n_pad * 4).
+ *   k_scales:         as q_scales with block_k.  MXFP4: uint8 E8M0 bytes
+ *                     [BH][n_pad/64][64][4] in the lane order of the score
+ *                     MFMA: for the 64-key tile t, byte 2*kb + h of entry
+ *                     32*g + r is the scale of key 64t + 32kb + r, channels
+ *                     64h + 32g .. 64h + 32g + 31 (k_scale_count = n_pad * 4).
  *   k_mean:           fp32 [BH][128] (mu).
  *   v_codes:          uint8 [BH][n_pad/64][128][64]: for each 64-key tile,
  *                     channel-major rows of 64 codes in a fixed key order:

@@ -24,6 +24,8 @@ QSDPA_ERR_ALIAS = -5
 QSDPA_ERR_HIP = -6
 QSDPA_QK_FP8_E4M3 = 0
 QSDPA_QK_FP4_E2M1 = 1
+QSDPA_QK_MXFP4_E2M1 = 2
+QK_FORMATS = {"fp8": QSDPA_QK_FP8_E4M3, "fp4": QSDPA_QK_FP4_E2M1, "mxfp4": QSDPA_QK_MXFP4_E2M1}
 HEAD_DIM = 128
 
 EXPORTS = ("qsdpa_abi_version", "qsdpa_status_string", "qsdpa_validate_params", "qsdpa_workspace_bytes",
@@ -97,11 +99,10 @@ def status_string(status: int) -> str:
 def make_params(batch: int, heads: int, seq_len: int, *, fmt: str = "fp8", block_q: int = 128,
                 block_k: int = 64, softmax_scale: float | None = None, head_dim: int = HEAD_DIM,
                 fp4_group: int = 16) -> QsdpaParams:
-    if fmt not in ("fp8", "fp4"):
-        raise ValueError(f"fmt must be 'fp8' or 'fp4', not {fmt!r}")
+    if fmt not in QK_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(QK_FORMATS)}, not {fmt!r}")
     tau = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
-    return QsdpaParams(batch, heads, seq_len, head_dim, block_q, block_k,
-                       QSDPA_QK_FP8_E4M3 if fmt == "fp8" else QSDPA_QK_FP4_E2M1, fp4_group, tau)
+    return QsdpaParams(batch, heads, seq_len, head_dim, block_q, block_k, QK_FORMATS[fmt], fp4_group, tau)
 
 
 def qsdpa_validate_params(params: QsdpaParams) -> int:

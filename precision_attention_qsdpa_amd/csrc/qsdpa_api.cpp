@@ -34,7 +34,7 @@ int check_params(const qsdpa_params* p) {
     if (p->block_k != 64) return QSDPA_ERR_UNSUPPORTED;
   } else if (p->qk_format == QSDPA_QK_FP4_E2M1) {
     if (p->fp4_group != 16) return QSDPA_ERR_UNSUPPORTED;
-  } else {
+  } else if (p->qk_format != QSDPA_QK_MXFP4_E2M1) {
     return QSDPA_ERR_UNSUPPORTED;
   }
   return QSDPA_OK;
@@ -45,18 +45,20 @@ void make_layout(const qsdpa_params* p, qsdpa_layout* L) {
   const uint64_t bh = (uint64_t)p->batch * p->heads;
   const int n_pad = (p->seq_len + 127) / 128 * 128;
   const bool fp4 = p->qk_format == QSDPA_QK_FP4_E2M1;
+  const bool mx = p->qk_format == QSDPA_QK_MXFP4_E2M1;
   L->n_pad = n_pad;
-  L->code_row_bytes = fp4 ? 64 : 128;
-  L->q_scale_count = fp4 ? n_pad * 8 : n_pad / p->block_q;
-  L->k_scale_count = fp4 ? n_pad * 8 : n_pad / 64;
+  L->code_row_bytes = fp4 || mx ? 64 : 128;
+  L->q_scale_count = fp4 ? n_pad * 8 : mx ? n_pad * 4 : n_pad / p->block_q;
+  L->k_scale_count = fp4 ? n_pad * 8 : mx ? n_pad * 4 : n_pad / 64;
+  const uint64_t scale_bytes = mx ? 1 : 4;   // E8M0 bytes or fp32
   L->stats_splits = (p->seq_len + qsdpa::STATS_ROWS - 1) / qsdpa::STATS_ROWS;
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) { const uint64_t at = off; off = align_up(off + bytes); return at; };
   L->q_codes = take(bh * n_pad * L->code_row_bytes);
   L->k_codes = take(bh * n_pad * L->code_row_bytes);
   L->v_codes = take(bh * n_pad * QSDPA_HEAD_DIM);
-  L->q_scales = take(bh * L->q_scale_count * 4);
-  L->k_scales = take(bh * L->k_scale_count * 4);
+  L->q_scales = take(bh * L->q_scale_count * scale_bytes);
+  L->k_scales = take(bh * L->k_scale_count * scale_bytes);
   L->k_mean = take(bh * QSDPA_HEAD_DIM * 4);
   L->v_scales = take(bh * QSDPA_HEAD_DIM * 4);
   L->v_amax = take(bh * QSDPA_HEAD_DIM * 4);
@@ -82,6 +84,7 @@ qsdpa::LaunchArgs make_args(const qsdpa_params* p, const qsdpa_layout& L, const 
   a.n_pad = L.n_pad;
   a.block_q = p->block_q;
   a.fp4 = p->qk_format == QSDPA_QK_FP4_E2M1;
+  a.mx = p->qk_format == QSDPA_QK_MXFP4_E2M1;
   a.softmax_scale = p->softmax_scale;
   a.stats_splits = L.stats_splits;
   a.q_scale_count = L.q_scale_count;

@@ -423,6 +423,193 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 kernel: the FP8 kernel's work split, tile ring, step schedule,
+// softmax and value product, with the scores on the scaled MFMA in its FP4
+// format.  Q and K arrive as E2M1 codes with one E8M0 scale per 32 channels,
+// and the MFMA applies those scales per lane (one byte per row or column and
+// 32-channel block), so the scores come out in real units and the softmax
+// constant is tau * log2(e) alone.  A K stage holds the tile's 4 KB of codes
+// (rows of 64 B; 16-byte chunk c of key row r stored at chunk
+// c ^ ((r >> 1) & 3)) and, per wave, a 1 KB copy of the tile's 256 scale
+// bytes (four replicas): each wave copies its own, so every wave issues the
+// same 4 copies per step and the ring's waits are those of the FP8 kernel.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int kmx_off(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 3)) << 4); }
+
+// score MFMA with FP4 A (K) and B (Q) operands: OA / OB select the scale byte
+template <int OA, int OB>
+__device__ __forceinline__ v16f mx_mfma(const v8i& a, const v8i& b, const v16f& c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, OA, (int)sa, OB, (int)sb);
+}
+__device__ __forceinline__ v8i lds_v4i(const uint8_t* p) {
+  const u32x4 a = *(const u32x4*)p;
+  return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+}
+
+__global__ __launch_bounds__(256, 2) void attn_mx_kernel(
+    const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
+    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * NSTAGE * KTILE];
+  auto lds_k = [&](int S) -> uint8_t* { return ring + S * KTILE; };
+  auto lds_v = [&](int S) -> uint8_t* { return ring + (NSTAGE + S) * KTILE; };
+  const uint32_t ring_lds = lds_addr(ring);
+  const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wave_lds = ring_lds + wave_u * 2048u;
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / tiles_per_bh, tile = wg - bh * tiles_per_bh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+  const int q0 = tile * QT + wave * QW;
+  const int T = (N + KSTEP - 1) / KSTEP;
+
+  // Q operand: 32 channels (16 bytes) of query q0 + r per 64-channel half h;
+  // its scale bytes (blocks g and 2 + g) in bytes 0 and 1 of qscale
+  v8i qb[2];
+  uint32_t qscale;
+  {
+    const size_t qrow = (size_t)bh * n_pad + q0 + r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qb[h] = lds_v4i(qc + qrow * 64 + 32 * h + 16 * g);
+    qscale = (uint32_t)qs[qrow * 4 + g] | ((uint32_t)qs[qrow * 4 + 2 + g] << 8);
+  }
+  const uint8_t* kbase = kc + (size_t)bh * n_pad * 64;
+  const uint8_t* ksbase = ks + (size_t)bh * (n_pad / KSTEP) * 256;
+  const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
+
+  // K operand of (kb, h): row kb*32 + r, chunk 2h + g; the swizzle depends on r only
+  int koff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) koff[h] = kmx_off(r, 2 * h + g);
+  const int voff0 = v_off(r, 2 * g), voff1 = v_off(r, 2 * g + 1);
+
+  // Ring copies.  K codes: wave w fills LDS chunks w*64 + lane of the stage
+  // with the global chunk the swizzle puts there; scale bytes: lane l reads
+  // bytes 16*(l & 15) .. +15 of the tile's 256, into the wave's own 1 KB.
+  uint32_t kg, sg, vg[2];
+  {
+    const int P = wave * 64 + lane, row = P >> 2, pc = P & 3;
+    kg = (uint32_t)(row * 64 + ((pc ^ ((row >> 1) & 3)) << 4));
+    sg = (uint32_t)((lane & 15) * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int Pv = (2 * wave + i) * 64 + lane;
+      const int d = Pv >> 2, pv = Pv & 3;
+      vg[i] = (uint32_t)(d * 64 + ((pv ^ ((d >> 2) & 3)) << 4));
+    }
+  }
+  auto ring_k = [&](int t, int S) {
+    ring_copy16(kbase + (size_t)t * 4096, kg, ring_lds + (uint32_t)S * KTILE + wave_u * 1024u);
+    ring_copy16(ksbase + (size_t)t * 256, sg, ring_lds + (uint32_t)S * KTILE + 4096u + wave_u * 1024u);
+  };
+  auto ring_v = [&](int t, int S) {
+    const uint8_t* tp = vbase + (size_t)t * KTILE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], wave_lds + (NSTAGE + S) * KTILE + i * 1024);
+  };
+
+  // the first score operand and the scale bytes, read by the caller ahead of
+  // the rescale: byte 2*kb + h of ksw scales K operand (kb, h)
+  auto k_first = [&](const uint8_t* kbuf) { return lds_v4i(kbuf + koff[0]); };
+  auto k_scales = [&](const uint8_t* kbuf) { return *(const uint32_t*)(kbuf + 4096 + wave * 1024 + lane * 4); };
+  auto scores = [&](const uint8_t* kbuf, v16f* s, const v8i& a00, uint32_t ksw) {
+    s[0] = mx_mfma<0, 0>(a00, qb[0], v16f{}, ksw, qscale);
+    s[0] = mx_mfma<1, 1>(lds_v4i(kbuf + koff[1]), qb[1], s[0], ksw, qscale);
+    s[1] = mx_mfma<2, 0>(lds_v4i(kbuf + 2048 + koff[0]), qb[0], v16f{}, ksw, qscale);
+    s[1] = mx_mfma<3, 1>(lds_v4i(kbuf + 2048 + koff[1]), qb[1], s[1], ksw, qscale);
+  };
+  v16f o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = v16f{};
+  float m = -INFINITY, l = 0.f;
+  auto softmax = [&](int t, v16f* s, auto full_t, float& alpha) -> v8i {
+    return softmax_step<decltype(full_t)::value>(s, tau_log2e, m, l, alpha, t * KSTEP, N, g);
+  };
+  auto rescale = [&](float alpha) { rescale_o(o, alpha); };
+  auto pv = [&](const v8i& pb, const uint8_t* vbuf) { value_mfma(o, pb, vbuf, voff0, voff1); };
+
+  // prologue as in the FP8 kernel
+  const int Tm1 = T - 1;
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+  ring_k(0, 0);
+  ring_k(min(1, Tm1), 1);
+  ring_k(min(2, Tm1), 2);
+  ring_k(min(3, Tm1), 3);
+  ring_v(0, 0);
+  ring_v(min(1, Tm1), 1);
+  *(u32x4*)(lds_v(3) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+  *(u32x4*)(lds_v(3) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
+  __builtin_amdgcn_s_waitcnt(0x0070 | 8);
+  asm volatile("s_barrier" ::: "memory");
+  v16f sa[2], sb[2];
+  scores(lds_k(0), sa, k_first(lds_k(0)), k_scales(lds_k(0)));
+  v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  float alpha_prev = 1.f;
+
+  auto step = [&](int t, v16f* s_cur, v16f* s_next, auto st) {
+    constexpr int S = decltype(st)::value;   // t % 4
+    const v8i a00 = k_first(lds_k((S + 1) & 3));
+    const uint32_t ksw = k_scales(lds_k((S + 1) & 3));
+    rescale(alpha_prev);
+    ring_k(min(t + 4, Tm1), S);
+    ring_v(min(t + 2, Tm1), (S + 2) & 3);
+    scores(lds_k((S + 1) & 3), s_next, a00, ksw);
+    pv(pb_prev, lds_v((S + 3) & 3));
+    pb_prev = softmax(t, s_cur, std::true_type{}, alpha_prev);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 22, 0);   // VALU
+    }
+    ring_barrier_wait8();
+  };
+  int t = 0;
+  for (; t + 4 < T; t += 4) {
+    step(t, sa, sb, std::integral_constant<int, 0>{});
+    step(t + 1, sb, sa, std::integral_constant<int, 1>{});
+    step(t + 2, sa, sb, std::integral_constant<int, 2>{});
+    step(t + 3, sb, sa, std::integral_constant<int, 3>{});
+  }
+  auto step_dyn = [&](int tt, v16f* s_cur, v16f* s_next) {
+    const int S = tt & 3;
+    const v8i a00 = k_first(lds_k((S + 1) & 3));
+    const uint32_t ksw = k_scales(lds_k((S + 1) & 3));
+    rescale(alpha_prev);
+    ring_k(min(tt + 4, Tm1), S);
+    ring_v(min(tt + 2, Tm1), (S + 2) & 3);
+    scores(lds_k((S + 1) & 3), s_next, a00, ksw);
+    pv(pb_prev, lds_v((S + 3) & 3));
+    pb_prev = softmax(tt, s_cur, std::true_type{}, alpha_prev);
+    ring_barrier_wait8();
+  };
+  auto last = [&](int tl, v16f* s_cur) {
+    const int S = tl & 3;
+    rescale(alpha_prev);
+    pv(pb_prev, lds_v((S + 3) & 3));
+    float alpha;
+    const v8i pb = (tl + 1) * KSTEP <= N ? softmax(tl, s_cur, std::true_type{}, alpha)
+                                         : softmax(tl, s_cur, std::false_type{}, alpha);
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+    rescale(alpha);
+    pv(pb, lds_v(S));
+  };
+  for (; t + 2 < T; t += 2) {
+    step_dyn(t, sa, sb);
+    step_dyn(t + 1, sb, sa);
+  }
+  if (t + 1 < T) {
+    step_dyn(t, sa, sb);
+    last(t + 1, sb);
+  } else {
+    last(t, sa);
+  }
+
+  const int q = q0 + r;
+  store_out(o, l, out, vs + (size_t)bh * D, (size_t)bh * N + q, q < N, g);
+}
+
+// ---------------------------------------------------------------------------
 // FP4 kernel: Q and K arrive as E2M1 codes with an fp32 scale per 16
 // channels.  Q is dequantized once into registers, and K comes as the f16
 // hi/lo tiles the quantize pass expanded (hi = f16(x), lo = f16(x - hi),
@@ -602,7 +789,11 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
   const int BH = a.batch * a.heads;
   const int tiles = a.n_pad / QT;
   const float tl = a.softmax_scale * LOG2E;
-  if (a.fp4) {
+  if (a.mx) {
+    attn_mx_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, (const uint8_t*)a.q_scales, a.k_codes,
+                                               (const uint8_t*)a.k_scales, a.v_codes, a.v_scales, (uint16_t*)a.o,
+                                               a.seq_len, a.n_pad, tl, tiles);
+  } else if (a.fp4) {
     attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded, a.v_codes, a.v_scales,
                                                 (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles);
   } else {

@@ -11,7 +11,8 @@ constexpr int STATS_ROWS = 256;  // tokens per range of the statistics pass
 struct LaunchArgs {
   int batch, heads, seq_len, n_pad;
   int block_q;
-  bool fp4;
+  bool fp4;   // 16-channel FP4 with fp32 scales
+  bool mx;    // MXFP4: 32-channel blocks with E8M0 scales
   float softmax_scale;
   int stats_splits;
   int q_scale_count, k_scale_count;

@@ -45,9 +45,17 @@ def read_workspace(ws: torch.Tensor, params, N: int) -> dict:
         out["k_scales"] = sec(L.k_scales, BH * L.k_scale_count, np.float32).reshape(B, H, -1)[:, :, :nk]
         out["q_scales_pad"] = sec(L.q_scales, BH * L.q_scale_count, np.float32).reshape(B, H, -1)[:, :, nq:]
         out["k_scales_pad"] = sec(L.k_scales, BH * L.k_scale_count, np.float32).reshape(B, H, -1)[:, :, nk:]
-    else:
+    elif params.qk_format == qs.QSDPA_QK_FP4_E2M1:
         out["q_scales"] = sec(L.q_scales, BH * L.q_scale_count, np.float32).reshape(B, H, L.n_pad, 8)[:, :, :N]
         out["k_scales"] = sec(L.k_scales, BH * L.k_scale_count, np.float32).reshape(B, H, L.n_pad, 8)[:, :, :N]
+    else:
+        # MXFP4: Q scale bytes token-major; K scale bytes in the score MFMA's lane
+        # order: tile t, entry 32g + r, byte 2kb + h -> key 64t + 32kb + r, block 2h + g
+        qsb = sec(L.q_scales, BH * L.q_scale_count, np.uint8).reshape(B, H, L.n_pad, 4)
+        ksl = sec(L.k_scales, BH * L.k_scale_count, np.uint8).reshape(B, H, L.n_pad // 64, 2, 32, 2, 2)  # t,g,r,kb,h
+        ksn = ksl.transpose(0, 1, 2, 5, 4, 6, 3).reshape(B, H, L.n_pad, 4)                          # t,kb,r,h,g
+        out["q_scales"], out["k_scales"] = qsb[:, :, :N], ksn[:, :, :N]
+        out["q_scales_pad"], out["k_scales_pad"] = qsb[:, :, N:], ksn[:, :, N:]
     out["k_mean"] = sec(L.k_mean, BH * 128, np.float32).reshape(B, H, 128)
     out["v_scales"] = sec(L.v_scales, BH * 128, np.float32).reshape(B, H, 128)
     out["v_amax"] = sec(L.v_amax, BH * 128, np.float32).reshape(B, H, 128)

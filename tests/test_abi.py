@@ -62,6 +62,12 @@ def test_fp4_group_checked_only_in_fp4_mode():
     assert qs.qsdpa_validate_params(p) == qs.QSDPA_OK
     p = qs.make_params(1, 1, 64, fmt="fp4", block_q=96)      # block sizes unused in FP4 mode
     assert qs.qsdpa_validate_params(p) == qs.QSDPA_OK
+    # MXFP4: fixed 32-channel blocks; block sizes and the FP4 group are not used
+    p = qs.make_params(1, 1, 64, fmt="mxfp4", block_q=96, block_k=32, fp4_group=7)
+    assert qs.qsdpa_validate_params(p) == qs.QSDPA_OK
+    p = qs.make_params(1, 1, 64, fmt="fp8")
+    p.qk_format = 3
+    assert qs.qsdpa_validate_params(p) == qs.QSDPA_ERR_UNSUPPORTED
 
 
 def _round(x, a):
@@ -70,19 +76,22 @@ def _round(x, a):
 
 @pytest.mark.parametrize("B,H,N,fmt,bq", [(1, 2, 320, "fp8", 64), (1, 24, 8704, "fp8", 128),
                                           (2, 24, 16896, "fp4", 128), (3, 5, 1, "fp8", 128),
-                                          (1, 1, 1000, "fp4", 64)])
+                                          (1, 1, 1000, "fp4", 64), (2, 24, 16896, "mxfp4", 128),
+                                          (1, 3, 77, "mxfp4", 64)])
 def test_workspace_closed_form(B, H, N, fmt, bq):
-    """One byte per Q/K code in FP8 mode (half a byte in FP4 mode), one byte per
-    V code, fp32 scales, padded to 128 tokens, 256-byte aligned sections; in
-    FP4 mode also the f16 hi/lo expansion of K (4 bytes per element)."""
+    """One byte per Q/K code in FP8 mode (half a byte in the FP4 modes), one byte
+    per V code, fp32 scales (one E8M0 byte per 32 channels in MXFP4 mode),
+    padded to 128 tokens, 256-byte aligned sections; in FP4 mode also the f16
+    hi/lo expansion of K (4 bytes per element)."""
     p = qs.make_params(B, H, N, fmt=fmt, block_q=bq)
     L = qs.qsdpa_workspace_layout(p)
     BH, npad = B * H, _round(N, 128)
     splits = -(-N // 256)
     crb = 128 if fmt == "fp8" else 64
-    qsc = npad // bq if fmt == "fp8" else npad * 8
-    ksc = npad // 64 if fmt == "fp8" else npad * 8
-    sizes = [BH * npad * crb, BH * npad * crb, BH * npad * 128, BH * qsc * 4, BH * ksc * 4,
+    qsc = {"fp8": npad // bq, "fp4": npad * 8, "mxfp4": npad * 4}[fmt]
+    ksc = {"fp8": npad // 64, "fp4": npad * 8, "mxfp4": npad * 4}[fmt]
+    sb = 1 if fmt == "mxfp4" else 4
+    sizes = [BH * npad * crb, BH * npad * crb, BH * npad * 128, BH * qsc * sb, BH * ksc * sb,
              BH * 512, BH * 512, BH * 512, BH * splits * 128 * 12,
              BH * npad * 128 * 4 if fmt == "fp4" else 0]
     assert (L.n_pad, L.code_row_bytes, L.q_scale_count, L.k_scale_count, L.stats_splits) == (npad, crb, qsc, ksc, splits)
@@ -95,7 +104,7 @@ def test_workspace_closed_form(B, H, N, fmt, bq):
     # FP8 halves the bf16 bytes of Q, K and V; FP4 Q/K codes (V stays FP8) cut them 3x
     qkv_bf16 = 3 * BH * N * 128 * 2
     codes = sizes[0] + sizes[1] + sizes[2]
-    assert (L.k_expanded == L.total) == (fmt == "fp8")
+    assert (L.k_expanded == L.total) == (fmt != "fp4")
     if N % 128 == 0:
         assert codes * (2 if fmt == "fp8" else 3) == qkv_bf16
 

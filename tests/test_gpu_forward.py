@@ -73,7 +73,7 @@ def test_forward_full_size(gpu_lib, name):
 
 
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 100, 127, 129, 1000])
-@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128)])
+@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128), ("mxfp4", 128)])
 def test_forward_ragged_lengths(gpu_lib, N, fmt, bq):
     qb, kb, vb = draw(WORKLOADS["tiny"], batch=2, heads=1, seq_len=N, seed=500 + N)
     params = qs.make_params(2, 1, N, fmt=fmt, block_q=bq)
@@ -82,7 +82,7 @@ def test_forward_ragged_lengths(gpu_lib, N, fmt, bq):
     compare(out, qb, kb, vb, fmt, bq, [(0, 0), (1, 0)], lambda b, h: np.arange(N), f"N={N} {fmt} bq={bq}")
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
 def test_zero_queries_closed_form(gpu_lib, fmt):
     """Q = 0: O is the mean of the dequantized V codes (every P code is 448)."""
     N = 1000

@@ -63,7 +63,7 @@ def test_quantize_bit_exact_full_size(gpu_lib, name):
 
 
 @pytest.mark.parametrize("N", [1, 63, 65, 100, 129, 1000])
-@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128)])
+@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128), ("mxfp4", 128)])
 def test_quantize_ragged_lengths(gpu_lib, N, fmt, bq):
     qb, kb, vb = draw(WORKLOADS["tiny"], batch=2, heads=2, seq_len=N, seed=77 + N)
     check_quantize(qb, kb, vb, fmt, bq, [(b, h) for b in range(2) for h in range(2)], f"N={N}")
@@ -75,5 +75,5 @@ def test_quantize_zero_blocks(gpu_lib):
     qb = qb.copy(); vb = vb.copy()
     qb[:, :, 64:128] = 0
     vb[:, :, :, 5] = 0
-    for fmt in ("fp8", "fp4"):
+    for fmt in ("fp8", "fp4", "mxfp4"):
         check_quantize(qb, kb, vb, fmt, 64, [(0, 0), (0, 1)], f"zero-{fmt}")

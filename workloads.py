@@ -62,6 +62,9 @@ WORKLOADS = {
     "kontext1024": Workload(4, "kontext1024", 1, 24, 8704, "fp8", 128, 64, 512, 4096, 4096),
     "gen2048_fp8": Workload(5, "gen2048_fp8", 2, 24, 16896, "fp8", 128, 64, 512, 16384),
     "gen2048_fp4": Workload(5, "gen2048_fp4", 2, 24, 16896, "fp4", 128, 64, 512, 16384),
+    # the same inputs in the MXFP4 mode (E8M0 scale per 32 channels, beyond the pages)
+    "kontext1024_mxfp4": Workload(4, "kontext1024_mxfp4", 1, 24, 8704, "mxfp4", 128, 64, 512, 4096, 4096),
+    "gen2048_mxfp4": Workload(5, "gen2048_mxfp4", 2, 24, 16896, "mxfp4", 128, 64, 512, 16384),
 }
 
 
