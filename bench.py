@@ -136,6 +136,11 @@ def main():
         if tj.get("workload") == w.name and tj.get("kernel_source_sha") == kernel_sha():
             traffic = tj.get("hbm_bytes_per_launch")
     elem = w.batch * w.heads * w.seq_len * 128
+    kernel = {"fp8": "attn_fp8_kernel", "fp4": "attn_fp4_kernel", "mxfp4": "attn_mx_kernel"}[w.fmt]
+    # quantize pass bytes per element: Q, K, V bf16 read (6) + K, V re-read by the
+    # statistics pass (4) + codes and scales written; FP4 mode also reads the K
+    # codes and scales again (0.75) and writes their f16 hi/lo expansion (4)
+    quant_bpe = {"fp8": 6 + 4 + 3, "fp4": 6 + 4 + 2 + 0.5 + 0.75 + 4, "mxfp4": 6 + 4 + 2 + 2 / 32}[w.fmt]
     rec = {
         "metric": "quantized SDPA TFLOPS at FLUX shapes (N=4608/8704/16896) + % FP8 MFMA peak",
         "value": round(tflops, 2),
@@ -147,16 +152,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if w.fmt == "fp8" else "fp4_e2m1+fp8_e4m3",
+        "dtype": {"fp8": "fp8_e4m3", "fp4": "fp4_e2m1+fp8_e4m3", "mxfp4": "mxfp4_e2m1+fp8_e4m3"}[w.fmt],
         "data": "synthetic (seeded N(0,1) Q/V, K with N(0,3) channel offsets; Kontext context tokens rho=0.8)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
                    "head_dim": 128, "qk_format": w.fmt, "block_q": w.block_q, "block_k": w.block_k,
                    "pct_fp8_peak": round(100.0 * tflops / FP8_PEAK_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel", "achieved": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
         "quantize": {"ms_per_launch": round(ms_quant, 4),
-                     "algorithmic_GB_s": round(elem * 13 / (ms_quant * 1e-3) / 1e9, 1),
+                     "algorithmic_GB_s": round(elem * quant_bpe / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_peak_GB_s": HBM_PEAK_GBS},
         "wall_s_timed": round(wall, 3),
     }
