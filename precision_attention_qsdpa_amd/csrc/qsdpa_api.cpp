@@ -85,6 +85,7 @@ qsdpa::LaunchArgs make_args(const qsdpa_params* p, const qsdpa_layout& L, const 
   a.block_q = p->block_q;
   a.fp4 = p->qk_format == QSDPA_QK_FP4_E2M1;
   a.mx = p->qk_format == QSDPA_QK_MXFP4_E2M1;
+  a.fuse_q = false;
   a.softmax_scale = p->softmax_scale;
   a.stats_splits = L.stats_splits;
   a.q_scale_count = L.q_scale_count;
@@ -201,7 +202,9 @@ int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const voi
   st = check_buffers(p, L, q, k, v, o, workspace, ws_bytes, true, true);
   if (st != QSDPA_OK) return st;
   (void)hipGetLastError();
-  const qsdpa::LaunchArgs a = make_args(p, L, q, k, v, o, workspace);
+  qsdpa::LaunchArgs a = make_args(p, L, q, k, v, o, workspace);
+  // FP8: Q is quantized inside the attention kernel, bit-identically
+  a.fuse_q = !a.fp4 && !a.mx;
   qsdpa::launch_quantize(a, (hipStream_t)stream);
   if (launch_status() != QSDPA_OK) return QSDPA_ERR_HIP;
   qsdpa::launch_attention(a, (hipStream_t)stream);

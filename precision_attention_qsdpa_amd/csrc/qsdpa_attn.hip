@@ -237,11 +237,16 @@ __device__ __forceinline__ void ring_barrier_wait8() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// FUSE_Q: Q comes as bf16 (qx) and this kernel computes its block scale and
+// codes in the prologue, with the operations of the quantize pass (same
+// block, same IEEE divisions, products and conversions), so the result is
+// bit-identical to quantizing Q first; qc and qs are then not read.
+template <bool FUSE_Q>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
-    const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kc,
-    const float* __restrict__ ks, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
-    uint16_t* __restrict__ out, int N, int n_pad, int block_q, int q_scale_count,
-    int k_scale_count, float tau_log2e, int tiles_per_bh) {
+    const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint16_t* __restrict__ qx,
+    const uint8_t* __restrict__ kc, const float* __restrict__ ks, const uint8_t* __restrict__ vc,
+    const float* __restrict__ vs, uint16_t* __restrict__ out, int N, int n_pad, int block_q,
+    int q_scale_count, int k_scale_count, float tau_log2e, int tiles_per_bh) {
   // ring: stages 0..3 of K tiles, then stages 0..3 of V^T tiles
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * NSTAGE * KTILE];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KTILE; };
@@ -257,12 +262,51 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   const int T = (N + KSTEP - 1) / KSTEP;
 
   v8i qb8[2];
-  {
+  float qscale;
+  if constexpr (FUSE_Q) {
+    // this lane's 64 channels of query q0 + r: 64h + 32g .. 64h + 32g + 31
+    float x[2][32];
+    float amax = 0.f;
+    const int q = q0 + r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (q < N) w = *(const u32x4*)(qx + ((size_t)bh * N + q) * D + 64 * h + 32 * g + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[h][8 * j + 2 * e] = bf16_lo(w[e]);
+          x[h][8 * j + 2 * e + 1] = bf16_hi(w[e]);
+        }
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[h][i]));
+    // the scale block: all 4 waves (block_q = 128) or this wave pair (64)
+    __shared__ float qred[4];
+    amax = wave_max(amax);
+    if (lane == 0) qred[wave] = amax;
+    __syncthreads();
+    amax = block_q == 128 ? fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3]))
+                          : fmaxf(qred[wave & 2], qred[(wave & 2) + 1]);
+    const float inv = amax > 0.f ? FP8_MAX / amax : 0.f;
+    qscale = amax > 0.f ? amax / FP8_MAX : 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int lo = cvt_e4m3x2<false>(clamp448(x[h][4 * j] * inv), clamp448(x[h][4 * j + 1] * inv), 0);
+        qb8[h][j] = cvt_e4m3x2<true>(clamp448(x[h][4 * j + 2] * inv), clamp448(x[h][4 * j + 3] * inv), lo);
+      }
+  } else {
     const uint8_t* qrow = qc + ((size_t)bh * n_pad + q0 + r) * D;
 #pragma unroll
     for (int h = 0; h < 2; ++h) qb8[h] = lds_v8i(qrow + 64 * h + 32 * g, qrow + 64 * h + 32 * g + 16);
+    qscale = qs[(size_t)bh * q_scale_count + q0 / block_q];
   }
-  const float cscale = tau_log2e * qs[(size_t)bh * q_scale_count + q0 / block_q];
+  const float cscale = tau_log2e * qscale;
   const uint8_t* kbase = kc + (size_t)bh * n_pad * D;
   const float* ksc = ks + (size_t)bh * k_scale_count;
   const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
@@ -797,9 +841,10 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
     attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded, a.v_codes, a.v_scales,
                                                 (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles);
   } else {
-    attn_fp8_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes,
-                                                a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,
-                                                a.q_scale_count, a.k_scale_count, tl, tiles);
+    auto kern = a.fuse_q ? attn_fp8_kernel<true> : attn_fp8_kernel<false>;
+    kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_codes, a.k_scales,
+                                    a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,
+                                    a.q_scale_count, a.k_scale_count, tl, tiles);
   }
 }
 

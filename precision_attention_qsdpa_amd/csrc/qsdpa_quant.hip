@@ -269,12 +269,12 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ mu, const float* __restrict__ vamax, uint8_t* __restrict__ qc,
     float* __restrict__ qs, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
-    int N, int n_pad) {
+    int N, int n_pad, int first_block) {
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * VROW];
   const int bh = blockIdx.y;
   const int qb = n_pad / BQ, kb = n_pad / KSTEP;
-  const int b = blockIdx.x;
+  const int b = blockIdx.x + first_block;   // first_block = qb: skip the Q blocks
   if (b < qb) {
     fp8_block<BQ>(q, nullptr, qc, qs + (size_t)bh * qb, N, n_pad, bh, b, red);
   } else if (b < qb + kb) {
@@ -413,14 +413,14 @@ void launch_quantize(const LaunchArgs& a, hipStream_t s) {
     expand_k_fp4_kernel<<<dim3(vtiles, BH), 256, 0, s>>>(a.k_codes, a.k_scales, a.k_expanded, a.n_pad);
     quant_v_kernel<<<dim3(vtiles, BH), 256, 0, s>>>((const uint16_t*)a.v, a.v_amax, a.v_codes, a.seq_len,
                                                    a.n_pad);
-  } else if (a.block_q == 128) {
-    quant_fp8_kernel<128><<<dim3(a.n_pad / 128 + a.n_pad / KSTEP + vtiles, BH), 256, 0, s>>>(
-        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean, a.v_amax, a.q_codes,
-        a.q_scales, a.k_codes, a.k_scales, a.v_codes, a.seq_len, a.n_pad);
   } else {
-    quant_fp8_kernel<64><<<dim3(a.n_pad / 64 + a.n_pad / KSTEP + vtiles, BH), 256, 0, s>>>(
-        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean, a.v_amax, a.q_codes,
-        a.q_scales, a.k_codes, a.k_scales, a.v_codes, a.seq_len, a.n_pad);
+    // Q blocks first (skipped when the attention kernel quantizes Q), then K blocks and V tiles
+    const int qblocks = a.n_pad / a.block_q, first = a.fuse_q ? qblocks : 0;
+    const dim3 grid(qblocks + a.n_pad / KSTEP + vtiles - first, BH);
+    auto kern = a.block_q == 128 ? quant_fp8_kernel<128> : quant_fp8_kernel<64>;
+    kern<<<grid, 256, 0, s>>>((const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean,
+                              a.v_amax, a.q_codes, a.q_scales, a.k_codes, a.k_scales, a.v_codes, a.seq_len,
+                              a.n_pad, first);
   }
 }
 

@@ -135,10 +135,18 @@ def test_deterministic_and_in_bounds(gpu_lib):
     assert torch.all(wbig[:4096] == 0x5A) and torch.all(wbig[4096 + need:] == 0x5A)
 
 
-def test_split_calls_equal_forward(gpu_lib):
-    """qsdpa_quantize + qsdpa_attention on a stream equals qsdpa_forward."""
-    qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=777, seed=31)
-    params = qs.make_params(1, 2, 777)
+@pytest.mark.parametrize("fmt,bq,N", [("fp8", 128, 777), ("fp8", 64, 777), ("fp8", 128, 1), ("fp8", 64, 100),
+                                       ("fp8", 128, 300), ("fp4", 128, 300), ("mxfp4", 128, 300)])
+def test_split_calls_equal_forward(gpu_lib, fmt, bq, N):
+    """qsdpa_quantize + qsdpa_attention on a stream equals qsdpa_forward bit for
+    bit (in FP8 mode the forward quantizes Q inside the attention kernel; one
+    Q block of the N = 300 cases is all zeros)."""
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=N, seed=31 + N)
+    if N == 300:
+        qb = qb.copy()
+        qb[:, :, 128:256] = 0
+    params = qs.make_params(1, 2, N, fmt=fmt, block_q=bq)
+    print(f"[forward] split vs fused fmt={fmt} bq={bq} N={N}", flush=True)
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
     ref = qs.qsdpa_forward(q, k, v, params=params)
     s = torch.cuda.Stream()
