@@ -110,18 +110,20 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # dominant kernel (fused attention) and the quantize pass, timed alone
+    # the quantize pass and the dominant kernel (fused attention), timed alone;
+    # the quantize pass runs first: it writes every workspace section the
+    # attention reads (qsdpa_forward leaves the Q codes to the attention kernel)
     n_attn = max(args.steps, 20)
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(n_attn):
-        qs.qsdpa_attention(ws, out, params, stream=stream)
-    a1.record(stream)
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for _ in range(n_attn):
         qs.qsdpa_quantize(q, k, v, ws, params, stream=stream)
     b1.record(stream)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(n_attn):
+        qs.qsdpa_attention(ws, out, params, stream=stream)
+    a1.record(stream)
     torch.cuda.synchronize(dev)
     ms_attn = a0.elapsed_time(a1) / n_attn
     ms_quant = b0.elapsed_time(b1) / n_attn
