@@ -1,7 +1,9 @@
-// Fused flash-style attention over the quantized workspace.  Two kernels:
-// attn_fp8_kernel (FP8 Q/K codes, asynchronous LDS ring) and attn_fp4_kernel
-// (FP4 Q/K codes dequantized to f16 hi/lo pairs).  What follows describes the
-// structure both share.
+// Fused flash-style attention over the quantized workspace.  Three kernels:
+// attn_fp8_kernel (FP8 Q/K codes, asynchronous LDS ring; optionally
+// quantizing Q itself from bf16), attn_mx_kernel (MXFP4 Q/K codes, scores on
+// the scaled MFMA in its FP4 format, same ring and schedule) and
+// attn_fp4_kernel (FP4 Q/K codes with fp32 scales per 16 channels, scores
+// from f16 hi/lo pairs).  What follows describes the structure all share.
 //
 // Work split: one workgroup = 4 waves = 128 consecutive queries of one (b,h);
 // each wave owns 32 queries and walks all keys in steps of 64, in ascending
@@ -27,9 +29,9 @@
 // 8 KB with a 16-byte-chunk XOR swizzle under which the 128-bit operand reads
 // show no LDS bank conflicts (SQ_LDS_BANK_CONFLICT = 0 on the Kontext shape).
 //
-// Numerics: scores are exact integer-valued FP8 dot products accumulated in
-// fp32 by the MFMA; one per-step constant c = tau*log2(e)*sQ*sK turns them
-// into base-2 logits; p*448 = exp2(s*c - m + log2 448); the running max m is
+// Numerics: scores are exact FP8 dot products accumulated in fp32 by the
+// MFMA; one per-step constant c = tau*log2(e)*sQ*sK (tau*log2(e) in MXFP4
+// mode, where the MFMA applies the scales) turns them into base-2 logits; p*448 = exp2(s*c - m + log2 448); the running max m is
 // taken over the exact per-step maxima; the rescale exp2(m_old - m_new) is
 // skipped when no lane's maximum moved (then it is exactly 1).
 #include <type_traits>
