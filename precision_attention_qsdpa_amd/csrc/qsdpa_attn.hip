@@ -264,51 +264,54 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   const int T = (N + KSTEP - 1) / KSTEP;
 
   v8i qb8[2];
-  float qscale;
-  if constexpr (FUSE_Q) {
-    // this lane's 64 channels of query q0 + r: 64h + 32g .. 64h + 32g + 31
-    float x[2][32];
-    float amax = 0.f;
-    const int q = q0 + r;
+  float qscale = 0.f;
+  auto load_q = [&]() {
+    if constexpr (FUSE_Q) {
+      // this lane's 64 channels of query q0 + r: 64h + 32g .. 64h + 32g + 31
+      float x[2][32];
+      float amax = 0.f;
+      const int q = q0 + r;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (q < N) w = *(const u32x4*)(qx + ((size_t)bh * N + q) * D + 64 * h + 32 * g + 8 * j);
+        for (int j = 0; j < 4; ++j) {
+          u32x4 w = {0u, 0u, 0u, 0u};
+          if (q < N) w = *(const u32x4*)(qx + ((size_t)bh * N + q) * D + 64 * h + 32 * g + 8 * j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[h][8 * j + 2 * e] = bf16_lo(w[e]);
-          x[h][8 * j + 2 * e + 1] = bf16_hi(w[e]);
+          for (int e = 0; e < 4; ++e) {
+            x[h][8 * j + 2 * e] = bf16_lo(w[e]);
+            x[h][8 * j + 2 * e + 1] = bf16_hi(w[e]);
+          }
         }
-      }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[h][i]));
-    // the scale block: all 4 waves (block_q = 128) or this wave pair (64)
-    __shared__ float qred[4];
-    amax = wave_max(amax);
-    if (lane == 0) qred[wave] = amax;
-    __syncthreads();
-    amax = block_q == 128 ? fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3]))
-                          : fmaxf(qred[wave & 2], qred[(wave & 2) + 1]);
-    const float inv = amax > 0.f ? FP8_MAX / amax : 0.f;
-    qscale = amax > 0.f ? amax / FP8_MAX : 0.f;
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[h][i]));
+      // the scale block: all 4 waves (block_q = 128) or this wave pair (64)
+      __shared__ float qred[4];
+      amax = wave_max(amax);
+      if (lane == 0) qred[wave] = amax;
+      __syncthreads();
+      amax = block_q == 128 ? fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3]))
+                            : fmaxf(qred[wave & 2], qred[(wave & 2) + 1]);
+      const float inv = amax > 0.f ? FP8_MAX / amax : 0.f;
+      qscale = amax > 0.f ? amax / FP8_MAX : 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int lo = cvt_e4m3x2<false>(clamp448(x[h][4 * j] * inv), clamp448(x[h][4 * j + 1] * inv), 0);
-        qb8[h][j] = cvt_e4m3x2<true>(clamp448(x[h][4 * j + 2] * inv), clamp448(x[h][4 * j + 3] * inv), lo);
-      }
-  } else {
-    const uint8_t* qrow = qc + ((size_t)bh * n_pad + q0 + r) * D;
+        for (int j = 0; j < 8; ++j) {
+          const int lo = cvt_e4m3x2<false>(clamp448(x[h][4 * j] * inv), clamp448(x[h][4 * j + 1] * inv), 0);
+          qb8[h][j] = cvt_e4m3x2<true>(clamp448(x[h][4 * j + 2] * inv), clamp448(x[h][4 * j + 3] * inv), lo);
+        }
+    } else {
+      const uint8_t* qrow = qc + ((size_t)bh * n_pad + q0 + r) * D;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) qb8[h] = lds_v8i(qrow + 64 * h + 32 * g, qrow + 64 * h + 32 * g + 16);
-    qscale = qs[(size_t)bh * q_scale_count + q0 / block_q];
-  }
-  const float cscale = tau_log2e * qscale;
+      for (int h = 0; h < 2; ++h) qb8[h] = lds_v8i(qrow + 64 * h + 32 * g, qrow + 64 * h + 32 * g + 16);
+      qscale = qs[(size_t)bh * q_scale_count + q0 / block_q];
+    }
+  };
+  if constexpr (!FUSE_Q) load_q();
+  float cscale = tau_log2e * qscale;   // FUSE_Q: set once Q is quantized in the prologue
   const uint8_t* kbase = kc + (size_t)bh * n_pad * D;
   const float* ksc = ks + (size_t)bh * k_scale_count;
   const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
@@ -378,15 +381,23 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
 
   // prologue: K(0..3) and V(0), V(1) in flight; V(-1) (stage 3) is zero.
   // The Q operand and scale loads complete first, so that from here on the
-  // only vector-memory loads in flight are ring copies.
+  // only vector-memory loads in flight are ring copies.  FUSE_Q issues the
+  // ring copies first and then loads and quantizes Q, so that both memory
+  // latencies overlap: its Q loads are younger than the copies, and loads
+  // complete in order, so the waits the compiler puts before using Q also
+  // cover the copies.
   const int Tm1 = T - 1;
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+  if constexpr (!FUSE_Q) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
   ring_k(0, 0);
   ring_k(min(1, Tm1), 1);
   ring_k(min(2, Tm1), 2);
   ring_k(min(3, Tm1), 3);
   ring_v(0, 0);
   ring_v(min(1, Tm1), 1);
+  if constexpr (FUSE_Q) {
+    load_q();
+    cscale = tau_log2e * qscale;
+  }
   *(u32x4*)(lds_v(3) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
   *(u32x4*)(lds_v(3) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
   // K(0), K(1) landed (at most K(2), K(3), V(0), V(1) outstanding)
