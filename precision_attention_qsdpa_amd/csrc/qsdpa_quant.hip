@@ -293,64 +293,89 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// MXFP4 codes: one thread per (token, 32-channel block).  grid = (n_pad/64,
-// BH, 2) (z = 0: Q, z = 1: smoothed K), block = 256 = 64 tokens x 4 blocks.
-// The shared scale is 2**(byte - 127) with byte = floor(log2 amax) - 2 + 127,
-// which for a normal fp32 amax is its exponent field minus 2 (0 below that or
-// for a zero block); x / 2**(byte - 127) is one exact fp32 multiply by the
-// power of two 2**(127 - byte), and the code is E2M1 of it, saturated at 6.
-// Codes [BH][n_pad][64] (even channel in the low nibble).  Q scale bytes
-// [BH][n_pad][4]; K scale bytes in the score MFMA's lane order: per 64-key
-// tile t, byte 2*kb + h of entry 32*g + r belongs to key 64t + 32kb + r and
-// channel block 2h + g.
+// MXFP4 codes of 64 tokens of Q (mu == nullptr) or of smoothed K.  Thread =
+// (row lane rl, 8-channel group cg): rows rl, rl+16, rl+32, rl+48, one 16-byte
+// load each; the 4 lanes of a 32-channel block (consecutive lanes) combine
+// their maxima with two xor shuffles.  The shared scale is 2**(byte - 127)
+// with byte = floor(log2 amax) - 2 + 127, which for a normal fp32 amax is its
+// exponent field minus 2 (0 below that or for a zero block); x / 2**(byte-127)
+// is one exact fp32 multiply by the power of two 2**(127 - byte), and the code
+// is E2M1 of it, saturated at 6.  Codes [BH][n_pad][64] (even channel in the
+// low nibble).  Q scale bytes [BH][n_pad][4]; K scale bytes in the score
+// MFMA's lane order: per 64-key tile t, byte 2*kb + h of entry 32*g + r
+// belongs to key 64t + 32kb + r and channel block 2h + g.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quant_qk_mx_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
-    uint8_t* __restrict__ qc, uint8_t* __restrict__ qs, uint8_t* __restrict__ kc,
-    uint8_t* __restrict__ ks, int N, int n_pad) {
-  const int bh = blockIdx.y;
-  const bool is_k = blockIdx.z == 1;
-  const uint16_t* x = is_k ? k : q;
-  const int tid = threadIdx.x, blk = tid & 3;
-  const int n = blockIdx.x * 64 + (tid >> 2);
-  float val[32];
-  float amax = 0.f;
-  if (n < N) {
-    const u32x4* src = (const u32x4*)(x + ((size_t)bh * N + n) * D + blk * 32);
+__device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, const float* __restrict__ mu,
+                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, bool lane_order,
+                                         int N, int n_pad, int bh, int blk) {
+  const int tid = threadIdx.x, cg = tid & 15, rl = tid >> 4;
+  float mloc[8];
+  if (mu) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 w = src[i];
+    for (int j = 0; j < 8; ++j) mloc[j] = mu[bh * D + cg * 8 + j];
+  }
+  float val[4][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        val[8 * i + 2 * j] = bf16_lo(w[j]);
-        val[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+  for (int i = 0; i < 4; ++i) {
+    const int n = blk * KSTEP + rl + 16 * i;
+    if (n < N) {
+      const u32x4 w = *(const u32x4*)(x + ((size_t)bh * N + n) * D + cg * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { val[i][2 * j] = bf16_lo(w[j]); val[i][2 * j + 1] = bf16_hi(w[j]); }
+      if (mu) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) val[i][j] = val[i][j] - mloc[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) val[i][j] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = blk * KSTEP + rl + 16 * i;
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(val[i][j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    uint32_t word = 0, byte = 0;
+    if (amax > 0.f) {
+      const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+      byte = (uint32_t)max(ex - 2, 0);
+      const float inv = __uint_as_float((254u - byte) << 23);   // 2**(127 - byte), a normal fp32
+#pragma unroll
+      for (int j = 0; j < 8; ++j) word |= e2m1_code(fminf(fmaxf(val[i][j] * inv, -FP4_MAX), FP4_MAX)) << (4 * j);
+    }
+    *(uint32_t*)(codes + ((size_t)bh * n_pad + n) * (D / 2) + cg * 4) = word;
+    if ((cg & 3) == 0) {
+      const int b = cg >> 2;
+      if (lane_order) {
+        const int t = n >> 6, kk = n & 63, kb = kk >> 5, r = kk & 31, h = b >> 1, g = b & 1;
+        scales[((size_t)bh * (n_pad / KSTEP) + t) * 256 + (32 * g + r) * 4 + 2 * kb + h] = (uint8_t)byte;
+      } else {
+        scales[((size_t)bh * n_pad + n) * 4 + b] = (uint8_t)byte;
       }
     }
-    if (is_k) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) val[j] = val[j] - mu[bh * D + blk * 32 + j];
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(val[j]));
   }
-  u32x4 out = {0u, 0u, 0u, 0u};
-  uint32_t byte = 0;
-  if (amax > 0.f) {
-    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-    byte = (uint32_t)max(ex - 2, 0);
-    const float inv = __uint_as_float((254u - byte) << 23);   // 2**(127 - byte), a normal fp32
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float y = fminf(fmaxf(val[j] * inv, -FP4_MAX), FP4_MAX);
-      out[j >> 3] |= e2m1_code(y) << (4 * (j & 7));
-    }
-  }
-  *(u32x4*)((is_k ? kc : qc) + ((size_t)bh * n_pad + n) * (D / 2) + blk * 16) = out;
-  if (is_k) {
-    const int t = n >> 6, kk = n & 63, kb = kk >> 5, r = kk & 31, h = blk >> 1, g = blk & 1;
-    ks[((size_t)bh * (n_pad / KSTEP) + t) * 256 + (32 * g + r) * 4 + 2 * kb + h] = (uint8_t)byte;
+}
+
+// MXFP4 mode: Q blocks, then K blocks, then V tiles, 64 tokens each, in one
+// grid = (3 * n_pad/64, BH); first_block = n_pad/64 skips the Q blocks.
+__global__ __launch_bounds__(256) void quant_mx_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ mu, const float* __restrict__ vamax, uint8_t* __restrict__ qc,
+    uint8_t* __restrict__ qs, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks, uint8_t* __restrict__ vc,
+    int N, int n_pad, int first_block) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * VROW];
+  const int bh = blockIdx.y, nb = n_pad / KSTEP;
+  const int b = blockIdx.x + first_block;
+  if (b < nb) {
+    mx_block(q, nullptr, qc, qs, false, N, n_pad, bh, b);
+  } else if (b < 2 * nb) {
+    mx_block(k, mu, kc, ks, true, N, n_pad, bh, b - nb);
   } else {
-    qs[((size_t)bh * n_pad + n) * 4 + blk] = (uint8_t)byte;
+    quant_v_tile(v, vamax, vc, N, n_pad, bh, b - 2 * nb, tile);
   }
 }
 
@@ -401,11 +426,9 @@ void launch_quantize(const LaunchArgs& a, hipStream_t s) {
                                         a.seq_len, a.stats_splits, a.k_mean, a.v_amax, a.v_scales);
   const int vtiles = a.n_pad / KSTEP;
   if (a.mx) {
-    quant_qk_mx_kernel<<<dim3(a.n_pad / 64, BH, 2), 256, 0, s>>>(
-        (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, (uint8_t*)a.q_scales, a.k_codes,
-        (uint8_t*)a.k_scales, a.seq_len, a.n_pad);
-    quant_v_kernel<<<dim3(vtiles, BH), 256, 0, s>>>((const uint16_t*)a.v, a.v_amax, a.v_codes, a.seq_len,
-                                                   a.n_pad);
+    quant_mx_kernel<<<dim3(3 * vtiles, BH), 256, 0, s>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean, a.v_amax, a.q_codes,
+        (uint8_t*)a.q_scales, a.k_codes, (uint8_t*)a.k_scales, a.v_codes, a.seq_len, a.n_pad, 0);
   } else if (a.fp4) {
     quant_qk_fp4_kernel<<<dim3(a.n_pad / 32, BH, 2), 256, 0, s>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
