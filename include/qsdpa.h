@@ -161,9 +161,9 @@ int qsdpa_attention(const qsdpa_params* p, const void* workspace, size_t ws_byte
 
 /*
  * qsdpa_quantize followed by qsdpa_attention on the same stream: O is
- * bit-identical to the two calls.  In FP8 mode the attention kernel
- * quantizes Q itself (the same blocks and operations), so the q_codes and
- * q_scales sections of the workspace are not written by this call.
+ * bit-identical to the two calls.  In FP8 and MXFP4 modes the attention
+ * kernel quantizes Q itself (the same blocks and operations), so the q_codes
+ * and q_scales sections of the workspace are not written by this call.
  */
 int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o,
                   void* workspace, size_t ws_bytes, void* stream);

@@ -203,8 +203,8 @@ int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const voi
   if (st != QSDPA_OK) return st;
   (void)hipGetLastError();
   qsdpa::LaunchArgs a = make_args(p, L, q, k, v, o, workspace);
-  // FP8: Q is quantized inside the attention kernel, bit-identically
-  a.fuse_q = !a.fp4 && !a.mx;
+  // FP8 and MXFP4: Q is quantized inside the attention kernel, bit-identically
+  a.fuse_q = !a.fp4;
   qsdpa::launch_quantize(a, (hipStream_t)stream);
   if (launch_status() != QSDPA_OK) return QSDPA_ERR_HIP;
   qsdpa::launch_attention(a, (hipStream_t)stream);

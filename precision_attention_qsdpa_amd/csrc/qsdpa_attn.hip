@@ -61,9 +61,14 @@ __device__ __forceinline__ v8i lds_v8i(const uint8_t* p0, const uint8_t* p1) {
 
 // max / sum of a value over the lane pair (l, l^32): one v_permlane32_swap
 // exchanges the two halves of the wave.
+// IEEE-754 maximum (v_maximum3_f32).  On the finite scores of the softmax it
+// gives the same value as fmaxf, whose maxnum semantics make the compiler
+// quiet each operand that is not known canonical (an MFMA result, a lane swap,
+// the running max) with an extra v_max_f32 x, x, x.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -103,15 +108,15 @@ __device__ __forceinline__ v8i softmax_step(v16f* s, float c, float& m, float& l
                                             int key0, int N, int g) {
   float m_new;
   if constexpr (FULL) {
-    float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-    float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+    float m0 = vmax(vmax(s[0][0], s[0][1]), s[0][2]);
+    float m1 = vmax(vmax(s[1][0], s[1][1]), s[1][2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) {
-      m0 = fmaxf(fmaxf(m0, s[0][i]), s[0][i + 1]);
-      m1 = fmaxf(fmaxf(m1, s[1][i]), s[1][i + 1]);
+      m0 = vmax(vmax(m0, s[0][i]), s[0][i + 1]);
+      m1 = vmax(vmax(m1, s[1][i]), s[1][i + 1]);
     }
-    const float mx = pair_max(fmaxf(fmaxf(m0, s[0][15]), fmaxf(m1, s[1][15])));
-    m_new = fmaxf(m, c * mx);
+    const float mx = pair_max(vmax(vmax(m0, s[0][15]), vmax(m1, s[1][15])));
+    m_new = vmax(m, c * mx);
     const float b = LOG2_448 - m_new;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -125,9 +130,9 @@ __device__ __forceinline__ v8i softmax_step(v16f* s, float c, float& m, float& l
       for (int i = 0; i < 16; ++i) {
         const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
         s[kb][i] = key < N ? s[kb][i] * c : -INFINITY;
-        mx = fmaxf(mx, s[kb][i]);
+        mx = vmax(mx, s[kb][i]);
       }
-    m_new = fmaxf(m, pair_max(mx));
+    m_new = vmax(m, pair_max(mx));
     const float b = LOG2_448 - m_new;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
       if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x402, 22, 0);         // VALU
+      __builtin_amdgcn_sched_group_barrier(0x402, 19, 0);         // VALU
     }
     kscn = ksc[t + 1];
     ring_barrier_wait8();
@@ -503,10 +508,15 @@ __device__ __forceinline__ v8i lds_v4i(const uint8_t* p) {
   return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
 }
 
+// FUSE_Q: Q arrives as bf16 (qx) and each lane quantizes its own two 32-channel
+// blocks in the prologue, with the quantize pass's operations, so the result
+// is bit-identical to reading the pass's codes (qc, qs).
+template <bool FUSE_Q>
 __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
-    const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
-    const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
-    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh) {
+    const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint16_t* __restrict__ qx,
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc,
+    const float* __restrict__ vs, uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e,
+    int tiles_per_bh) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * NSTAGE * KTILE];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KTILE; };
   auto lds_v = [&](int S) -> uint8_t* { return ring + (NSTAGE + S) * KTILE; };
@@ -520,16 +530,51 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
   const int q0 = tile * QT + wave * QW;
   const int T = (N + KSTEP - 1) / KSTEP;
 
-  // Q operand: 32 channels (16 bytes) of query q0 + r per 64-channel half h;
-  // its scale bytes (blocks g and 2 + g) in bytes 0 and 1 of qscale
+  // Q operand: channels 64h + 32g .. +31 (scale block 2h + g) of query q0 + r
+  // as 16 bytes of codes per half h; the two scale bytes in bytes 0 and 1 of
+  // qscale
   v8i qb[2];
-  uint32_t qscale;
-  {
-    const size_t qrow = (size_t)bh * n_pad + q0 + r;
+  uint32_t qscale = 0u;
+  auto load_q = [&]() {
+    if constexpr (FUSE_Q) {
+      const int q = q0 + r;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) qb[h] = lds_v4i(qc + qrow * 64 + 32 * h + 16 * g);
-    qscale = (uint32_t)qs[qrow * 4 + g] | ((uint32_t)qs[qrow * 4 + 2 + g] << 8);
-  }
+      for (int h = 0; h < 2; ++h) {
+        float x[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x4 w = {0u, 0u, 0u, 0u};
+          if (q < N) w = *(const u32x4*)(qx + ((size_t)bh * N + q) * D + 64 * h + 32 * g + 8 * j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[8 * j + 2 * e] = bf16_lo(w[e]);
+            x[8 * j + 2 * e + 1] = bf16_hi(w[e]);
+          }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        const uint32_t byte = amax > 0.f ? mx_scale_byte(amax) : 0u;
+        const float inv = mx_inv_scale(byte);
+        int words[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t wd = 0u;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wd |= mx_code(x[8 * j + e], inv) << (4 * e);
+          words[j] = amax > 0.f ? (int)wd : 0;
+        }
+        qb[h] = v8i{words[0], words[1], words[2], words[3], 0, 0, 0, 0};
+        qscale |= byte << (8 * h);
+      }
+    } else {
+      const size_t qrow = (size_t)bh * n_pad + q0 + r;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) qb[h] = lds_v4i(qc + qrow * 64 + 32 * h + 16 * g);
+      qscale = (uint32_t)qs[qrow * 4 + g] | ((uint32_t)qs[qrow * 4 + 2 + g] << 8);
+    }
+  };
+  if constexpr (!FUSE_Q) load_q();
   const uint8_t* kbase = kc + (size_t)bh * n_pad * 64;
   const uint8_t* ksbase = ks + (size_t)bh * (n_pad / KSTEP) * 256;
   const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
@@ -585,15 +630,16 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
   auto rescale = [&](float alpha) { rescale_o(o, alpha); };
   auto pv = [&](const v8i& pb, const uint8_t* vbuf) { value_mfma(o, pb, vbuf, voff0, voff1); };
 
-  // prologue as in the FP8 kernel
+  // prologue as in the FP8 kernel (FUSE_Q: Q loaded after the ring copies)
   const int Tm1 = T - 1;
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+  if constexpr (!FUSE_Q) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
   ring_k(0, 0);
   ring_k(min(1, Tm1), 1);
   ring_k(min(2, Tm1), 2);
   ring_k(min(3, Tm1), 3);
   ring_v(0, 0);
   ring_v(min(1, Tm1), 1);
+  if constexpr (FUSE_Q) load_q();
   *(u32x4*)(lds_v(3) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
   *(u32x4*)(lds_v(3) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
   __builtin_amdgcn_s_waitcnt(0x0070 | 8);
@@ -847,9 +893,10 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
   const int tiles = a.n_pad / QT;
   const float tl = a.softmax_scale * LOG2E;
   if (a.mx) {
-    attn_mx_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, (const uint8_t*)a.q_scales, a.k_codes,
-                                               (const uint8_t*)a.k_scales, a.v_codes, a.v_scales, (uint16_t*)a.o,
-                                               a.seq_len, a.n_pad, tl, tiles);
+    auto kern = a.fuse_q ? attn_mx_kernel<true> : attn_mx_kernel<false>;
+    kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, (const uint8_t*)a.q_scales, (const uint16_t*)a.q, a.k_codes,
+                                    (const uint8_t*)a.k_scales, a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len,
+                                    a.n_pad, tl, tiles);
   } else if (a.fp4) {
     attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded, a.v_codes, a.v_scales,
                                                 (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles);

@@ -51,6 +51,20 @@ __device__ __forceinline__ uint32_t e2m1_code(float x) {
   return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// MXFP4 (OCP Microscaling v1.0): the E8M0 byte shared by a block of 32
+// values whose largest magnitude amax > 0 is 2 below amax's biased exponent
+// (2 is E2M1's largest exponent), at least 0; the codes are E2M1 of
+// x * 2^(127 - byte), saturating at 6.  The inverse scale 2^(127 - byte) is a
+// normal fp32, so x * inv is exact; a block with amax = 0 keeps byte 0 and
+// all-zero codes (callers skip the codes there).
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  return (uint32_t)max((int)((__float_as_uint(amax) >> 23) & 0xffu) - 2, 0);
+}
+__device__ __forceinline__ float mx_inv_scale(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
+__device__ __forceinline__ uint32_t mx_code(float x, float inv) {
+  return e2m1_code(fminf(fmaxf(x * inv, -FP4_MAX), FP4_MAX));
+}
+
 // Value of an E2M1 code (sign bit 3, exponent bits 2..1, mantissa bit 0).
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
   const uint32_t e = (c >> 1) & 3u, m = c & 1u;

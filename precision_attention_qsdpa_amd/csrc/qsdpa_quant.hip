@@ -341,11 +341,10 @@ __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, const f
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     uint32_t word = 0, byte = 0;
     if (amax > 0.f) {
-      const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-      byte = (uint32_t)max(ex - 2, 0);
-      const float inv = __uint_as_float((254u - byte) << 23);   // 2**(127 - byte), a normal fp32
+      byte = mx_scale_byte(amax);
+      const float inv = mx_inv_scale(byte);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) word |= e2m1_code(fminf(fmaxf(val[i][j] * inv, -FP4_MAX), FP4_MAX)) << (4 * j);
+      for (int j = 0; j < 8; ++j) word |= mx_code(val[i][j], inv) << (4 * j);
     }
     *(uint32_t*)(codes + ((size_t)bh * n_pad + n) * (D / 2) + cg * 4) = word;
     if ((cg & 3) == 0) {
@@ -426,9 +425,11 @@ void launch_quantize(const LaunchArgs& a, hipStream_t s) {
                                         a.seq_len, a.stats_splits, a.k_mean, a.v_amax, a.v_scales);
   const int vtiles = a.n_pad / KSTEP;
   if (a.mx) {
-    quant_mx_kernel<<<dim3(3 * vtiles, BH), 256, 0, s>>>(
+    // Q blocks skipped when the attention kernel quantizes Q
+    const int first = a.fuse_q ? vtiles : 0;
+    quant_mx_kernel<<<dim3(3 * vtiles - first, BH), 256, 0, s>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean, a.v_amax, a.q_codes,
-        (uint8_t*)a.q_scales, a.k_codes, (uint8_t*)a.k_scales, a.v_codes, a.seq_len, a.n_pad, 0);
+        (uint8_t*)a.q_scales, a.k_codes, (uint8_t*)a.k_scales, a.v_codes, a.seq_len, a.n_pad, first);
   } else if (a.fp4) {
     quant_qk_fp4_kernel<<<dim3(a.n_pad / 32, BH, 2), 256, 0, s>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,

@@ -136,11 +136,12 @@ def test_deterministic_and_in_bounds(gpu_lib):
 
 
 @pytest.mark.parametrize("fmt,bq,N", [("fp8", 128, 777), ("fp8", 64, 777), ("fp8", 128, 1), ("fp8", 64, 100),
-                                       ("fp8", 128, 300), ("fp4", 128, 300), ("mxfp4", 128, 300)])
+                                       ("fp8", 128, 300), ("fp4", 128, 300), ("mxfp4", 128, 300),
+                                       ("mxfp4", 128, 777), ("mxfp4", 128, 1)])
 def test_split_calls_equal_forward(gpu_lib, fmt, bq, N):
     """qsdpa_quantize + qsdpa_attention on a stream equals qsdpa_forward bit for
-    bit (in FP8 mode the forward quantizes Q inside the attention kernel; one
-    Q block of the N = 300 cases is all zeros)."""
+    bit (in FP8 and MXFP4 modes the forward quantizes Q inside the attention
+    kernel; one Q block of the N = 300 cases is all zeros)."""
     qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=N, seed=31 + N)
     if N == 300:
         qb = qb.copy()
