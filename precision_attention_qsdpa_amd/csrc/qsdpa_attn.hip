@@ -558,12 +558,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
         const float inv = mx_inv_scale(byte);
         int words[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t wd = 0u;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) wd |= mx_code(x[8 * j + e], inv) << (4 * e);
-          words[j] = amax > 0.f ? (int)wd : 0;
-        }
+        for (int j = 0; j < 4; ++j) words[j] = amax > 0.f ? (int)e2m1_word8(x + 8 * j, inv) : 0;
         qb[h] = v8i{words[0], words[1], words[2], words[3], 0, 0, 0, 0};
         qscale |= byte << (8 * h);
       }

@@ -41,14 +41,17 @@ __device__ __forceinline__ int cvt_e4m3x2(float a, float b, int old) {
 
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -FP8_MAX), FP8_MAX); }
 
-// E2M1 code of fp32 x with |x| <= 6, round to nearest even, sign kept.
-// Magnitude thresholds: ties at 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 go to
-// the neighbour with an even mantissa bit.
-__device__ __forceinline__ uint32_t e2m1_code(float x) {
-  float y = fabsf(x);
-  uint32_t c = (y > 0.25f) + (y >= 0.75f) + (y > 1.25f) + (y >= 1.75f) + (y > 2.5f) +
-               (y >= 3.5f) + (y > 5.0f);
-  return c | ((__float_as_uint(x) >> 28) & 8u);
+// E2M1 codes of the eight fp32 values v[0..7] * inv, each clamped to
+// [-6, 6], four bytes with v[2k] in the low nibble of byte k.  The hardware
+// conversion (v_cvt_scalef32_pk_fp4_f32 at scale 1) rounds to nearest even
+// and keeps the sign: ties 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2,
+// 2.5 -> 2, 3.5 -> 4, 5 -> 4 go to the even mantissa, and -0 gives code 8.
+__device__ __forceinline__ float clamp6(float x) { return __builtin_amdgcn_fmed3f(x, -FP4_MAX, FP4_MAX); }
+__device__ __forceinline__ uint32_t e2m1_word8(const float* v, float inv) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, clamp6(v[0] * inv), clamp6(v[1] * inv), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp6(v[2] * inv), clamp6(v[3] * inv), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp6(v[4] * inv), clamp6(v[5] * inv), 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp6(v[6] * inv), clamp6(v[7] * inv), 1.0f, 3);
 }
 
 // MXFP4 (OCP Microscaling v1.0): the E8M0 byte shared by a block of 32
@@ -61,9 +64,6 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
   return (uint32_t)max((int)((__float_as_uint(amax) >> 23) & 0xffu) - 2, 0);
 }
 __device__ __forceinline__ float mx_inv_scale(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
-__device__ __forceinline__ uint32_t mx_code(float x, float inv) {
-  return e2m1_code(fminf(fmaxf(x * inv, -FP4_MAX), FP4_MAX));
-}
 
 // Value of an E2M1 code (sign bit 3, exponent bits 2..1, mantissa bit 0).
 __device__ __forceinline__ float e2m1_value(uint32_t c) {

@@ -186,11 +186,8 @@ __global__ __launch_bounds__(256) void quant_qk_fp4_kernel(
   if (amax > 0.f) {
     const float inv = FP4_MAX / amax;
     scale = amax / FP4_MAX;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float y = fminf(fmaxf(val[j] * inv, -FP4_MAX), FP4_MAX);
-      out[j >> 3] |= e2m1_code(y) << (4 * (j & 7));
-    }
+    out[0] = e2m1_word8(val, inv);
+    out[1] = e2m1_word8(val + 8, inv);
   }
   *(u32x2*)(codes + ((size_t)bh * n_pad + n) * (D / 2) + grp * 8) = out;
   scales[((size_t)bh * n_pad + n) * 8 + grp] = scale;
@@ -343,8 +340,7 @@ __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, const f
     if (amax > 0.f) {
       byte = mx_scale_byte(amax);
       const float inv = mx_inv_scale(byte);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) word |= mx_code(val[i][j], inv) << (4 * j);
+      word = e2m1_word8(val[i], inv);
     }
     *(uint32_t*)(codes + ((size_t)bh * n_pad + n) * (D / 2) + cg * 4) = word;
     if ((cg & 3) == 0) {

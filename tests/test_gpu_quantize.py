@@ -77,3 +77,41 @@ def test_quantize_zero_blocks(gpu_lib):
     vb[:, :, :, 5] = 0
     for fmt in ("fp8", "fp4", "mxfp4"):
         check_quantize(qb, kb, vb, fmt, 64, [(0, 0), (0, 1)], f"zero-{fmt}")
+
+
+def e2m1_tie_rows(rng, n_rows):
+    """Rows of 128 bf16-exact values in which every 16-channel group holds
+    magnitude 6 once, so that both FP4 scalings are exactly 1 (fp32 scale
+    6/6, MXFP4 exponent byte 127), and whose other values sit on the E2M1
+    rounding ties, one bf16 step either side of them, on the code values and
+    on signed zeros."""
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    pool = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0] + ties
+    for t in ties:
+        ulp = 2.0 ** (np.floor(np.log2(t)) - 7)          # bf16 spacing at t
+        pool += [t - ulp, t + ulp]
+    pool = np.array(pool, dtype=np.float32)
+    rows = np.empty((n_rows, 128), dtype=np.float32)
+    for i in range(n_rows):
+        for grp in range(8):
+            vals = rng.choice(pool, 16) * rng.choice(np.array([-1.0, 1.0], np.float32), 16)
+            vals[rng.integers(16)] = rng.choice(np.array([-6.0, 6.0], np.float32))
+            rows[i, 16 * grp:16 * grp + 16] = vals
+    bits = rows.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "values must be exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "mxfp4"])
+def test_quantize_e2m1_ties(gpu_lib, fmt):
+    """E2M1 encoding at its rounding ties: Q and K values whose scaled value
+    is exactly a tie, a neighbour of one, a code value or a signed zero.  K's
+    token n + 64 is -K's token n, so its channel means are exactly 0 and the
+    smoothing leaves it unchanged."""
+    rng = np.random.default_rng(2024)
+    N = 128
+    qb = e2m1_tie_rows(rng, N).reshape(1, 1, N, 128)
+    kh = e2m1_tie_rows(rng, N // 2)
+    kb = np.concatenate([kh, kh ^ np.uint16(0x8000)]).reshape(1, 1, N, 128)
+    _, _, vb = draw(WORKLOADS["tiny"], heads=1, seq_len=N, seed=9)
+    check_quantize(qb, kb, vb, fmt, 128, [(0, 0)], f"ties-{fmt}")
