@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define QSDPA_ABI_VERSION 2
+#define QSDPA_ABI_VERSION 3
 #define QSDPA_HEAD_DIM 128
 
 /* Status codes (return values). */
@@ -110,12 +110,16 @@ typedef struct qsdpa_params {
  *   v_scales:         fp32 [BH][128] (sV).
  *   v_amax:           fp32 [BH][128] (vmax).
  *   stats:            scratch for partial channel sums (fp64) and maxima.
- *   k_expanded:       FP4 mode only (0 bytes in FP8 mode): every K element
- *                     x = code * scale split into f16 hi = f16(x) and
- *                     lo = f16(x - hi), both rounded to nearest even, as
- *                     f16 [BH][n_pad/64][2][64][128]: per 64-key tile the
- *                     hi tile, then the lo tile; in a key row the 8-channel
+ *   k_expanded:       FP4 mode only (0 bytes in other modes): every K
+ *                     element x = code * scale (one fp32 product) times
+ *                     2^-E of its 64-key tile, split into f16 hi = f16(x')
+ *                     and lo = f16(x' - hi), both rounded to nearest even,
+ *                     as f16 [BH][n_pad/64][2][64][128]: per tile the hi
+ *                     tile, then the lo tile; in a key row the 8-channel
  *                     chunk c is stored at chunk position c ^ (key & 15).
+ *                     Then int32 E [BH][n_pad/64]: E = e - 138, e the
+ *                     biased exponent field of the largest K scale of the
+ *                     tile, so |x'| < 24576 and hi/lo never overflow f16.
  */
 typedef struct qsdpa_layout {
   uint64_t q_codes, q_scales, k_codes, k_scales, k_mean, v_codes, v_scales, v_amax, stats;

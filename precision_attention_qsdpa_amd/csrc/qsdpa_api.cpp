@@ -63,7 +63,7 @@ void make_layout(const qsdpa_params* p, qsdpa_layout* L) {
   L->v_scales = take(bh * QSDPA_HEAD_DIM * 4);
   L->v_amax = take(bh * QSDPA_HEAD_DIM * 4);
   L->stats = take(bh * L->stats_splits * QSDPA_HEAD_DIM * (8 + 4));
-  L->k_expanded = take(fp4 ? bh * n_pad * QSDPA_HEAD_DIM * 4 : 0);
+  L->k_expanded = take(fp4 ? bh * n_pad * QSDPA_HEAD_DIM * 4 + bh * (n_pad / 64) * 4 : 0);
   L->total = off;
 }
 

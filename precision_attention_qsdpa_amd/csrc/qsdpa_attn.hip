@@ -30,10 +30,11 @@
 // show no LDS bank conflicts (SQ_LDS_BANK_CONFLICT = 0 on the Kontext shape).
 //
 // Numerics: scores are exact FP8 dot products accumulated in fp32 by the
-// MFMA; one per-step constant c = tau*log2(e)*sQ*sK (tau*log2(e) in MXFP4
-// mode, where the MFMA applies the scales) turns them into base-2 logits; p*448 = exp2(s*c - m + log2 448); the running max m is
-// taken over the exact per-step maxima; the rescale exp2(m_old - m_new) is
-// skipped when no lane's maximum moved (then it is exactly 1).
+// MFMA; one per-step constant c = tau*log2(e)*sQ*sK >= 0 (tau*log2(e) in
+// MXFP4 mode, where the MFMA applies the scales) turns them into base-2
+// logits; p*448 = exp2(s*c - m + log2 448); the running max m is taken over
+// the exact per-step maxima; the rescale exp2(m_old - m_new) is skipped when
+// no lane's maximum moved (then it is exactly 1).
 #include <type_traits>
 
 #include "qsdpa_device.h"
@@ -59,13 +60,13 @@ __device__ __forceinline__ v8i lds_v8i(const uint8_t* p0, const uint8_t* p1) {
   return r;
 }
 
-// max / sum of a value over the lane pair (l, l^32): one v_permlane32_swap
-// exchanges the two halves of the wave.
 // IEEE-754 maximum (v_maximum3_f32).  On the finite scores of the softmax it
 // gives the same value as fmaxf, whose maxnum semantics make the compiler
 // quiet each operand that is not known canonical (an MFMA result, a lane swap,
 // the running max) with an extra v_max_f32 x, x, x.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// max / sum of a value over the lane pair (l, l^32): one v_permlane32_swap
+// exchanges the two halves of the wave.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -94,7 +95,7 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
 
 
 // ---------------------------------------------------------------------------
-// Pieces shared by both kernels
+// Pieces shared by the kernels
 // ---------------------------------------------------------------------------
 
 // Online softmax of one 64-key step for the 32 raw scores a lane holds (two
@@ -203,8 +204,7 @@ __device__ __forceinline__ void store_out(const v16f* o, float l, uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// FP8 kernel with asynchronous tile loads.  Same work split, layouts and
-// softmax as attn_kernel, but K and V^T tiles go from HBM/L2 straight into LDS
+// FP8 kernel.  K and V^T tiles go from HBM/L2 straight into LDS
 // (global_load_lds_dwordx4: no registers, no LDS store instructions) through
 // a ring of 4 stages, issued 3 steps before they are read:
 //   step t reads K(t+1) (scores of step t+1) and V(t-1) (values of step t-1)
@@ -713,7 +713,9 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
 // hi/lo tiles the quantize pass expanded (hi = f16(x), lo = f16(x - hi),
 // about 2^-22 relative), so the scores are three f16 MFMAs per 16-channel
 // chunk (hi.hi + lo.hi + hi.lo) and keep fp32-level accuracy while P and V
-// stay FP8.  The tiles reach LDS as in the FP8 kernel, by asynchronous copies
+// stay FP8.  Before the split, a query row is scaled by 2^-EQ and a K tile by
+// 2^-EK (fp4_norm_exp), which keeps every f16 in range; the softmax constant
+// tau * log2(e) * 2^(EQ + EK) of the lane and step takes both back.  The tiles reach LDS as in the FP8 kernel, by asynchronous copies
 // (global_load_lds_dwordx4), through a ring of 3 stages of 32 KB K + 8 KB V^T
 // issued 2 steps before they are read:
 //   step t reads K(t+1) and V(t-1), and issues K(t+3) and V(t+1);
@@ -731,8 +733,8 @@ __device__ __forceinline__ void ring_barrier_wait10() {
 
 __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kx,
-    const uint8_t* __restrict__ vc, const float* __restrict__ vs, uint16_t* __restrict__ out, int N,
-    int n_pad, float tau_log2e, int tiles_per_bh) {
+    const int* __restrict__ kexp, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
+    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh) {
   // ring: stages 0..2 of expanded K tiles (hi then lo), then stages 0..2 of V^T tiles
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE4 * (KXTILE + KTILE)];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KXTILE; };
@@ -746,23 +748,36 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
   const int q0 = tile * QT + wave * QW;
   const int T = (N + KSTEP - 1) / KSTEP;
 
-  // Q operand: chunk c covers channels 16c + 8g .. 16c + 8g + 7 of query q0 + r
+  // Q operand: chunk c covers channels 16c + 8g .. 16c + 8g + 7 of query q0 + r,
+  // scaled by 2^-EQ of the query row (both lanes of the row read all 8 scales);
+  // the softmax constant of the lane takes 2^EQ back
   v8h qhi[8], qlo[8];
+  float cq;
   {
     const size_t qrow = (size_t)bh * n_pad + q0 + r;
+    float sc[8], smax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      sc[c] = qs[qrow * 8 + c];
+      smax = fmaxf(smax, sc[c]);
+    }
+    const int EQ = fp4_norm_exp(smax);
+    cq = ldexpf(tau_log2e, EQ);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t w = *(const uint32_t*)(qc + qrow * 64 + 8 * c + 4 * g);
-      const float s = qs[qrow * 8 + c];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = e2m1_value((w >> (4 * e)) & 15u) * s;
+        float x = e2m1_value((w >> (4 * e)) & 15u) * sc[c];
+        asm volatile("" : "+v"(x));
+        x = ldexpf(x, -EQ);
         qhi[c][e] = (_Float16)x;
         qlo[c][e] = (_Float16)(x - (float)qhi[c][e]);
       }
     }
   }
   const uint8_t* kxbase = kx + (size_t)bh * (n_pad / KSTEP) * KXTILE;
+  const int* kebase = kexp + (size_t)bh * (n_pad / KSTEP);
   const uint8_t* vbase = vc + (size_t)bh * n_pad * D;
   const int voff0 = v_off(r, 2 * g), voff1 = v_off(r, 2 * g + 1);
 
@@ -817,6 +832,10 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
   for (int i = 0; i < 4; ++i) o[i] = v16f{};
   float m = -INFINITY, l = 0.f;
 
+  // K-tile exponent of the step whose softmax runs next, loaded before each
+  // barrier wait (as the FP8 kernel's K scale)
+  int ken = kebase[0];
+
   // prologue: K(0..2) and V(0) in flight; V(-1) (stage 2) is zero.  The Q
   // operand loads complete first, so that from here on the only vector-memory
   // loads in flight are ring copies.
@@ -843,12 +862,13 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
     ring_v(min(t + 1, Tm1), S1);
     scores(lds_k(S1), s_next);
     value_mfma(o, pb_prev, lds_v(S2), voff0, voff1);
-    pb_prev = softmax_step<true>(s_cur, tau_log2e, m, l, alpha_prev, t * KSTEP, N, g);
+    pb_prev = softmax_step<true>(s_cur, ldexpf(cq, ken), m, l, alpha_prev, t * KSTEP, N, g);
 #pragma unroll
     for (int i = 0; i < 52; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);   // VALU
     }
+    ken = kebase[t + 1];
     ring_barrier_wait10();
   };
   int t = 0, S = 0;
@@ -864,9 +884,9 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
     rescale_o(o, alpha_prev);
     value_mfma(o, pb_prev, lds_v(S2), voff0, voff1);
     float alpha;
-    const v8i pb = (tl + 1) * KSTEP <= N
-                       ? softmax_step<true>(s_cur, tau_log2e, m, l, alpha, tl * KSTEP, N, g)
-                       : softmax_step<false>(s_cur, tau_log2e, m, l, alpha, tl * KSTEP, N, g);
+    const float c = ldexpf(cq, ken);
+    const v8i pb = (tl + 1) * KSTEP <= N ? softmax_step<true>(s_cur, c, m, l, alpha, tl * KSTEP, N, g)
+                                         : softmax_step<false>(s_cur, c, m, l, alpha, tl * KSTEP, N, g);
     __builtin_amdgcn_s_waitcnt(0x0070);   // every ring copy has landed
     asm volatile("s_barrier" ::: "memory");
     rescale_o(o, alpha);
@@ -893,8 +913,11 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
                                     (const uint8_t*)a.k_scales, a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len,
                                     a.n_pad, tl, tiles);
   } else if (a.fp4) {
-    attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded, a.v_codes, a.v_scales,
-                                                (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles);
+    const int ktiles = a.n_pad / KSTEP;
+    attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded,
+                                                (const int*)(a.k_expanded + (size_t)BH * ktiles * KXTILE),
+                                                a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl,
+                                                tiles);
   } else {
     auto kern = a.fuse_q ? attn_fp8_kernel<true> : attn_fp8_kernel<false>;
     kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_codes, a.k_scales,

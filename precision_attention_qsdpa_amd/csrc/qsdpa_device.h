@@ -72,6 +72,16 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
   return (c & 8u) ? -mag : mag;
 }
 
+// FP4 mode: the power of two 2^-E that brings the dequantized values of a
+// query row or a 64-key K tile into f16's range before their hi/lo split:
+// E = e - 138, e the biased exponent field of the largest fp32 scale (0 for
+// zero or subnormal scales).  smax < 2^(e - 126), so the largest magnitude
+// 6 * smax * 2^-E stays below 0.75 * 2^15 = 24576 (f16's largest finite value
+// is 65504), and values more than 2^28 below it are still f16 normals.
+// x * 2^-E is exact (ldexp), so the split keeps its relative precision
+// whatever the input magnitude.
+__device__ __forceinline__ int fp4_norm_exp(float smax) { return (int)((__float_as_uint(smax) >> 23) & 0xffu) - 138; }
+
 // Bytes of one 64-key tile of FP4-mode K expanded to f16 hi + lo (2 x 16 KB),
 // and the byte offset of 8-channel chunk c of key row `row` inside the hi (or
 // lo) half: rows of 256 B, chunk c stored at position c ^ (row & 15), so the

@@ -376,31 +376,50 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
 
 // ---------------------------------------------------------------------------
 // FP4 mode: K expanded once per head for the attention kernel's score MFMAs.
-// Each element x = code * scale becomes hi = f16(x) and lo = f16(x - hi)
-// (both round to nearest even; hi + lo carries x to about 2^-22 relative),
-// written as 32 KB per 64-key tile in the LDS order the attention kernel
-// reads, so that it can copy tiles into LDS unchanged.  grid = (n_pad/64, BH),
-// block = 256; a thread expands 4 of the tile's 64 x 16 chunks of 8 channels.
+// Each element x = code * scale, times the tile's power of two 2^-E
+// (fp4_norm_exp of the tile's largest scale), becomes hi = f16(x') and
+// lo = f16(x' - hi) (both round to nearest even; hi + lo carries x' to about
+// 2^-22 relative), written as 32 KB per 64-key tile in the LDS order the
+// attention kernel reads, so that it can copy tiles into LDS unchanged; E
+// goes to kexp[tile].  grid = (n_pad/64, BH), block = 256; a thread expands
+// 4 of the tile's 64 x 16 chunks of 8 channels.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void expand_k_fp4_kernel(const uint8_t* __restrict__ kc,
                                                            const float* __restrict__ ks,
-                                                           uint8_t* __restrict__ kx, int n_pad) {
-  const int tile = blockIdx.x, bh = blockIdx.y;
-  uint8_t* dst = kx + ((size_t)bh * (n_pad / KSTEP) + tile) * KXTILE;
+                                                           uint8_t* __restrict__ kx, int* __restrict__ kexp,
+                                                           int n_pad) {
+  __shared__ float wmax[4];
+  const int tile = blockIdx.x, bh = blockIdx.y, tiles = n_pad / KSTEP;
+  uint8_t* dst = kx + ((size_t)bh * tiles + tile) * KXTILE;
+  uint32_t w[4];
+  float s[4], smax = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = threadIdx.x + 256 * i;
     const int key = idx >> 4, c = idx & 15;
     const size_t row = (size_t)bh * n_pad + (size_t)tile * KSTEP + key;
-    const uint32_t w = *(const uint32_t*)(kc + row * (D / 2) + 4 * c);
-    const float s = ks[row * 8 + (c >> 1)];
+    w[i] = *(const uint32_t*)(kc + row * (D / 2) + 4 * c);
+    s[i] = ks[row * 8 + (c >> 1)];
+    smax = fmaxf(smax, s[i]);
+  }
+  smax = wave_max(smax);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = smax;
+  __syncthreads();
+  const int E = fp4_norm_exp(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+  if (threadIdx.x == 0) kexp[(size_t)bh * tiles + tile] = E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    const int key = idx >> 4, c = idx & 15;
     v8h hv, lv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = e2m1_value((w >> (4 * e)) & 15u) * s;
-      // x rounded to fp32 first (no fused multiply-convert), so that hi and
-      // lo are exactly f16(x) and f16(x - hi), signed zeros included
+      // x rounded to fp32 first (no fused multiply-convert), then scaled
+      // exactly, so that hi and lo are f16(x') and f16(x' - hi), signed zeros
+      // included
+      float x = e2m1_value((w[i] >> (4 * e)) & 15u) * s[i];
       asm volatile("" : "+v"(x));
+      x = ldexpf(x, -E);
       hv[e] = (_Float16)x;
       lv[e] = (_Float16)(x - (float)hv[e]);
     }
@@ -430,7 +449,8 @@ void launch_quantize(const LaunchArgs& a, hipStream_t s) {
     quant_qk_fp4_kernel<<<dim3(a.n_pad / 32, BH, 2), 256, 0, s>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
         a.k_scales, a.seq_len, a.n_pad);
-    expand_k_fp4_kernel<<<dim3(vtiles, BH), 256, 0, s>>>(a.k_codes, a.k_scales, a.k_expanded, a.n_pad);
+    expand_k_fp4_kernel<<<dim3(vtiles, BH), 256, 0, s>>>(a.k_codes, a.k_scales, a.k_expanded,
+                                                        (int*)(a.k_expanded + (size_t)BH * vtiles * KXTILE), a.n_pad);
     quant_v_kernel<<<dim3(vtiles, BH), 256, 0, s>>>((const uint16_t*)a.v, a.v_amax, a.v_codes, a.seq_len,
                                                    a.n_pad);
   } else {

@@ -76,6 +76,9 @@ def read_workspace(ws: torch.Tensor, params, N: int) -> dict:
         nat = nat.reshape(B, H, L.n_pad // 64, 2, 64, 128).transpose(0, 1, 3, 2, 4, 5).reshape(B, H, 2, L.n_pad, 128)
         out["k_hi"], out["k_lo"] = nat[:, :, 0, :N], nat[:, :, 1, :N]
         out["k_hilo_pad"] = nat[:, :, :, N:]
+        # then the power-of-two exponent E of each tile (int32 [B, H, n_pad/64])
+        out["k_exp"] = sec(L.k_expanded + BH * L.n_pad * 512, BH * (L.n_pad // 64), np.int32).reshape(
+            B, H, L.n_pad // 64)
     return out
 
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 2
+    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 3
     for st in range(-6, 1):
         assert qs.status_string(st) not in ("", "unknown status")
     assert qs.status_string(-99) == "unknown status"
@@ -82,7 +82,8 @@ def test_workspace_closed_form(B, H, N, fmt, bq):
     """One byte per Q/K code in FP8 mode (half a byte in the FP4 modes), one byte
     per V code, fp32 scales (one E8M0 byte per 32 channels in MXFP4 mode),
     padded to 128 tokens, 256-byte aligned sections; in FP4 mode also the f16
-    hi/lo expansion of K (4 bytes per element)."""
+    hi/lo expansion of K (4 bytes per element) and an int32 exponent per 64-key
+    tile."""
     p = qs.make_params(B, H, N, fmt=fmt, block_q=bq)
     L = qs.qsdpa_workspace_layout(p)
     BH, npad = B * H, _round(N, 128)
@@ -93,7 +94,7 @@ def test_workspace_closed_form(B, H, N, fmt, bq):
     sb = 1 if fmt == "mxfp4" else 4
     sizes = [BH * npad * crb, BH * npad * crb, BH * npad * 128, BH * qsc * sb, BH * ksc * sb,
              BH * 512, BH * 512, BH * 512, BH * splits * 128 * 12,
-             BH * npad * 128 * 4 if fmt == "fp4" else 0]
+             BH * npad * 128 * 4 + BH * (npad // 64) * 4 if fmt == "fp4" else 0]
     assert (L.n_pad, L.code_row_bytes, L.q_scale_count, L.k_scale_count, L.stats_splits) == (npad, crb, qsc, ksc, splits)
     assert L.total == sum(_round(s, 256) for s in sizes)
     assert qs.qsdpa_workspace_bytes(p) == L.total

@@ -159,3 +159,33 @@ def test_split_calls_equal_forward(gpu_lib, fmt, bq, N):
     s.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
+def scale_bits(bits, e):
+    """bf16 bit patterns times 2^e (exact for the normal values used here)."""
+    x = np.ldexp((bits.astype(np.uint32) << 16).view(np.float32), e).astype(np.float32)
+    u = x.view(np.uint32)
+    assert np.all(u & 0xFFFF == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+@pytest.mark.parametrize("shift", [14, -14])
+def test_power_of_two_input_scaling(gpu_lib, fmt, shift):
+    """Q times 2^shift and K times 2^-shift leave every score unchanged (the
+    scales absorb the powers of two exactly, and so does K's mean), so O is
+    bit-identical to the unscaled run.  At shift 14 |Q| (and at -14 |K|) goes
+    past 65504, the largest f16: this holds only because the FP4 mode
+    normalizes query rows and key tiles before its f16 hi/lo split."""
+    N = 300
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=N, seed=44)
+    params = qs.make_params(1, 2, N, fmt=fmt, block_q=128)
+    print(f"[forward] power-of-two scaling fmt={fmt} shift={shift}", flush=True)
+    ref = run_forward(qb, kb, vb, params)
+    qs_, ks_ = scale_bits(qb, shift), scale_bits(kb, -shift)
+    big = (qs_ if shift > 0 else ks_).astype(np.uint32) << 16
+    assert np.abs(big.view(np.float32)).max() > 65504.0
+    got = run_forward(qs_, ks_, vb, params)
+    assert np.array_equal(got, ref)
+    compare(got, qs_, ks_, vb, fmt, 128, [(0, 0), (0, 1)], lambda b, h: np.arange(N),
+            f"scaled-{fmt}-{shift}")

@@ -40,9 +40,18 @@ def check_quantize(qb, kb, vb, fmt, block_q, heads, label):
                 bad = np.argwhere(g.reshape(want.shape) != want)
                 pytest.fail(f"{label} {name} (b={b},h={h}): {len(bad)} mismatches, first at {bad[:3].tolist()}")
         if fmt == "fp4":
-            # the f16 pair the FP4 score MFMAs take: hi = f16(x), lo = f16(x - hi) in fp32,
-            # x = fp32 of the oracle's exact code * scale
+            # the f16 pair the FP4 score MFMAs take: x = fp32 of the oracle's exact
+            # code * scale, times 2^-E of its 64-key tile (E = biased exponent of the
+            # tile's largest scale - 138, as documented in include/qsdpa.h), then
+            # hi = f16(x), lo = f16(x - hi) in fp32
             x = oracle.dequantize_qk(z.k_codes, z.k_scales, fmt, 16, 0, 0).astype(np.float32)
+            sk = np.zeros((got["k_exp"].shape[2] * 64, 8), np.float32)
+            sk[:N] = z.k_scales[0, 0]
+            smax = sk.reshape(-1, 64 * 8).max(axis=1)
+            E = ((smax.view(np.uint32) >> 23) & 0xFF).astype(np.int32) - 138
+            if not np.array_equal(got["k_exp"][b, h], E):
+                pytest.fail(f"{label} k_exp (b={b},h={h}): {got['k_exp'][b, h][:8]} != {E[:8]}")
+            x = np.ldexp(x, -np.repeat(E, 64)[:N, None]).astype(np.float32)
             hi = x.astype(np.float16)
             lo = (x - hi.astype(np.float32)).astype(np.float16)
             for name, want in (("k_hi", hi), ("k_lo", lo)):
