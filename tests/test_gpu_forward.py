@@ -72,6 +72,22 @@ def test_forward_full_size(gpu_lib, name):
     compare(out, qb, kb, vb, w.fmt, w.block_q, heads, rows_of, name)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "fp4"])
+def test_forward_long_sequence(gpu_lib, fmt):
+    """One head of 131109 tokens (7.8x the longest workload, with a ragged last
+    step): 2049 online-softmax steps and 1025 query tiles, checked on sampled
+    rows of the first, middle and last tiles."""
+    N = (1 << 17) + 37
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=1, seq_len=N, seed=262)
+    params = qs.make_params(1, 1, N, fmt=fmt, block_q=128)
+    print(f"[forward] long sequence N={N} fmt={fmt}", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128], [N // 2, N // 2 + 31], [N - 128, N - 37, N - 2, N - 1],
+                                     rng.choice(N, 6, replace=False)]))
+    compare(out, qb, kb, vb, fmt, 128, [(0, 0)], lambda b, h: rows, f"long-{fmt}")
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 100, 127, 129, 1000])
 @pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128), ("mxfp4", 128)])
 def test_forward_ragged_lengths(gpu_lib, N, fmt, bq):
