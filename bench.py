@@ -7,7 +7,9 @@ Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line: TFLOP/s of the whole step (4 B H N^2 D per step), the
 roofline of the dominant kernel (the fused attention, timed with HIP events
-on the stream it runs on) and the CPU oracle timed on a bounded sample.
+on the stream it runs on), the CPU oracle timed on a bounded sample, and the
+GPU output's error against that oracle sample and against exact fp64
+attention of the unquantized inputs.
 """
 from __future__ import annotations
 
@@ -41,25 +43,55 @@ def parse():
 
 def cpu_baseline(w, heads: int):
     """The oracle, single process with single-threaded BLAS, on the first
-    ``heads`` (b, h) pairs of the workload: quantize of each head and every
-    query row against every key."""
+    ``heads`` (b, h) pairs of batch 0 of the workload: quantize of each head
+    and every query row against every key.  Returns the record and the
+    oracle's outputs [heads, N, 128] (fp64 values of bf16)."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
     from workloads import TAU, draw
 
-    qb, kb, vb = draw(w, batch=1, heads=heads)
+    qb, kb, vb = draw(w, batch=1, heads=heads)   # the same tensors as heads 0.. of batch 0
+    outs = np.empty((heads, w.seq_len, 128))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         for h in range(heads):
             z = oracle.quantize(qb[:, h:h + 1], kb[:, h:h + 1], vb[:, h:h + 1], fmt=w.fmt,
                                 block_q=w.block_q, block_k=w.block_k)
-            oracle.attend(z, TAU, 0, 0)
+            outs[h] = oracle.attend(z, TAU, 0, 0)
         dt = time.perf_counter() - t0
     flops = 4.0 * heads * w.seq_len ** 2 * 128
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of the {w.batch * w.heads} (b,h) pairs of {w.name}, all {w.seq_len} query rows "
-                      f"(quantize + attention), {dt:.1f} s wall, single-threaded NumPy"}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+           "sample": f"{heads} of the {w.batch * w.heads} (b,h) pairs of {w.name}, all {w.seq_len} query rows "
+                     f"(quantize + attention), {dt:.1f} s wall, single-threaded NumPy"}
+    return rec, outs, (qb, kb, vb)
+
+
+def accuracy(w, got_bits, want, inputs, rows_per_head: int = 256):
+    """Error of the GPU output (bf16 bits [heads, N, 128] of batch 0) against
+    the oracle's output on the same heads, and against exact fp64 softmax
+    attention of the unquantized inputs on sampled rows."""
+    import numpy as np
+
+    import oracle
+    from workloads import TAU
+
+    got = oracle.bf16_bits_to_f64(got_bits)
+    d = np.abs(got - want)
+    qb, kb, vb = inputs
+    rng = np.random.default_rng(0)
+    ex = []
+    for h in range(want.shape[0]):
+        rows = np.sort(rng.choice(w.seq_len, min(rows_per_head, w.seq_len), replace=False))
+        q, k, v = (oracle.bf16_bits_to_f64(x[0, h]) for x in (qb, kb, vb))
+        ex.append(np.abs(got[h, rows] - oracle.exact_attention(q, k, v, TAU, rows)))
+    e = np.concatenate([x.ravel() for x in ex])
+    return {"vs_oracle": {"max_abs": float(d.max()), "mean_abs": float(d.mean()),
+                          "sample": f"{want.shape[0]} heads x {w.seq_len} rows"},
+            "vs_exact_fp64": {"max_abs": float(e.max()), "mean_abs": float(e.mean()),
+                              "sample": f"{want.shape[0]} heads x {min(rows_per_head, w.seq_len)} rows"},
+            "tolerance_vs_oracle": {"max_abs": 1e-2, "mean_abs": 1e-3}}
 
 
 def main():
@@ -168,7 +200,10 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+        heads = min(args.cpu_heads, w.heads)
+        got_bits = out[0, :heads].contiguous().view(torch.int16).cpu().numpy().view("uint16")
+        rec["cpu_baseline"], want, inputs = cpu_baseline(w, heads)
+        rec["accuracy"] = accuracy(w, got_bits, want, inputs)
     print(json.dumps(rec), flush=True)
 
 
