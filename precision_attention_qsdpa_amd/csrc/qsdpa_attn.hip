@@ -492,11 +492,11 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
 // 32-channel block), so the scores come out in real units and the softmax
 // constant is tau * log2(e) alone.  A K stage holds the tile's 4 KB of codes
 // (rows of 64 B; 16-byte chunk c of key row r stored at chunk
-// c ^ ((r >> 1) & 3)) and, per wave, a 1 KB copy of the tile's 256 scale
+// c ^ ((r >> 2) & 3), as in a V^T tile) and, per wave, a 1 KB copy of the tile's 256 scale
 // bytes (four replicas): each wave copies its own, so every wave issues the
 // same 4 copies per step and the ring's waits are those of the FP8 kernel.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int kmx_off(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 3)) << 4); }
+__device__ __forceinline__ int kmx_off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
 // score MFMA with FP4 A (K) and B (Q) operands: OA / OB select the scale byte
 template <int OA, int OB>
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
   uint32_t kg, sg, vg[2];
   {
     const int P = wave * 64 + lane, row = P >> 2, pc = P & 3;
-    kg = (uint32_t)(row * 64 + ((pc ^ ((row >> 1) & 3)) << 4));
+    kg = (uint32_t)(row * 64 + ((pc ^ ((row >> 2) & 3)) << 4));
     sg = (uint32_t)((lane & 15) * 16);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
