@@ -35,6 +35,7 @@
 // logits; p*448 = exp2(s*c - m + log2 448); the running max m is taken over
 // the exact per-step maxima; the rescale exp2(m_old - m_new) is skipped when
 // no lane's maximum moved (then it is exactly 1).
+#include <atomic>
 #include <type_traits>
 
 #include "qsdpa_device.h"
@@ -82,6 +83,21 @@ __device__ __forceinline__ int undef_int() {
   int x;
   asm volatile("" : "=v"(x));
   return x;
+}
+
+// Issue priority by dispatch round.  Workgroups start in id order as slots
+// free up, `slots` at a time (two per CU), and a SIMD's arbiter favours its
+// older wave: the younger of two only takes the cycles the older leaves
+// idle.  Near the end of the grid that makes the last workgroups, which start
+// beside an older one and carry the most remaining work, crawl until their
+// partner finishes and then run alone.  With s_setprio 3 for the last round
+// and 1 for the one before (the best of the level patterns measured), the
+// later workgroup leads instead: Kontext FP8 attention 2.3 % faster, MXFP4
+// 2.5 %.
+__device__ __forceinline__ void set_round_priority(int slots) {
+  const int round = (int)blockIdx.x / slots, last = ((int)gridDim.x - 1) / slots;
+  if (round == last) __builtin_amdgcn_s_setprio(3);
+  else if (round == last - 1) __builtin_amdgcn_s_setprio(1);
 }
 
 // Maps the hardware workgroup id so that each XCD (ids are dealt round-robin
@@ -253,7 +269,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint16_t* __restrict__ qx,
     const uint8_t* __restrict__ kc, const float* __restrict__ ks, const uint8_t* __restrict__ vc,
     const float* __restrict__ vs, uint16_t* __restrict__ out, int N, int n_pad, int block_q,
-    int q_scale_count, int k_scale_count, float tau_log2e, int tiles_per_bh) {
+    int q_scale_count, int k_scale_count, float tau_log2e, int tiles_per_bh, int prio_slots) {
+  set_round_priority(prio_slots);
   // ring: stages 0..3 of K tiles, then stages 0..3 of V^T tiles
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * NSTAGE * KTILE];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KTILE; };
@@ -516,7 +533,8 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint16_t* __restrict__ qx,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc,
     const float* __restrict__ vs, uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e,
-    int tiles_per_bh) {
+    int tiles_per_bh, int prio_slots) {
+  set_round_priority(prio_slots);
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * NSTAGE * KTILE];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KTILE; };
   auto lds_v = [&](int S) -> uint8_t* { return ring + (NSTAGE + S) * KTILE; };
@@ -903,15 +921,30 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
   store_out(o, l, out, vs + (size_t)bh * D, (size_t)bh * N + q, q < N, g);
 }
 
+// Compute units of the current device, read once per device (an immutable
+// property); 256 if the query fails.
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 void launch_attention(const LaunchArgs& a, hipStream_t s) {
   const int BH = a.batch * a.heads;
+  const int slots = 2 * device_cus();   // two workgroups of the FP8 and MXFP4 kernels per CU
   const int tiles = a.n_pad / QT;
   const float tl = a.softmax_scale * LOG2E;
   if (a.mx) {
     auto kern = a.fuse_q ? attn_mx_kernel<true> : attn_mx_kernel<false>;
     kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, (const uint8_t*)a.q_scales, (const uint16_t*)a.q, a.k_codes,
                                     (const uint8_t*)a.k_scales, a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len,
-                                    a.n_pad, tl, tiles);
+                                    a.n_pad, tl, tiles, slots);
   } else if (a.fp4) {
     const int ktiles = a.n_pad / KSTEP;
     attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded,
@@ -922,7 +955,7 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
     auto kern = a.fuse_q ? attn_fp8_kernel<true> : attn_fp8_kernel<false>;
     kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_codes, a.k_scales,
                                     a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,
-                                    a.q_scale_count, a.k_scale_count, tl, tiles);
+                                    a.q_scale_count, a.k_scale_count, tl, tiles, slots);
   }
 }
 
