@@ -733,30 +733,25 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
 // chunk (hi.hi + lo.hi + hi.lo) and keep fp32-level accuracy while P and V
 // stay FP8.  Before the split, a query row is scaled by 2^-EQ and a K tile by
 // 2^-EK (fp4_norm_exp), which keeps every f16 in range; the softmax constant
-// tau * log2(e) * 2^(EQ + EK) of the lane and step takes both back.  The tiles reach LDS as in the FP8 kernel, by asynchronous copies
-// (global_load_lds_dwordx4), through a ring of 3 stages of 32 KB K + 8 KB V^T
-// issued 2 steps before they are read:
-//   step t reads K(t+1) and V(t-1), and issues K(t+3) and V(t+1);
-// each wave issues 10 copies per step, so at the end of step t it waits until
-// at most 10 are outstanding (those of step t): K(t+2) and V(t) have landed.
-// One wave per SIMD: the f16 Q operand alone takes 64 registers.
+// tau * log2(e) * 2^(EQ + EK) of the lane and step takes both back.
+// The tiles reach LDS as in the FP8 kernel, by asynchronous copies
+// (global_load_lds_dwordx4), through a ring of 2 stages of 32 KB K + 8 KB V^T:
+// 80 KB, so that two workgroups share a CU and two waves share each SIMD.
+// The f16 Q operand alone takes 64 registers, so a wave has one scores
+// buffer: its softmax and its MFMAs alternate, and the other wave of the SIMD
+// fills the gaps (MFMA 72 % busy at 2048^2, against 51 % with one wave per
+// SIMD, three stages and double-buffered scores).
 // ---------------------------------------------------------------------------
-constexpr int NSTAGE4 = 3;
-
-__device__ __forceinline__ void ring_barrier_wait10() {
-  // s_waitcnt vmcnt(10) lgkmcnt(0), then the barrier
-  __builtin_amdgcn_s_waitcnt(0x0070 | 10);
-  asm volatile("s_barrier" ::: "memory");
-}
-
-__global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
+__global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kx,
     const int* __restrict__ kexp, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
-    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh) {
-  // ring: stages 0..2 of expanded K tiles (hi then lo), then stages 0..2 of V^T tiles
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE4 * (KXTILE + KTILE)];
+    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh, int prio_slots) {
+  set_round_priority(prio_slots);
+  // ring: stages 0, 1 of expanded K tiles (hi then lo), then stages 0, 1 of V^T tiles: 80 KB,
+  // so that two workgroups share a CU's 160 KB
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * (KXTILE + KTILE)];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KXTILE; };
-  auto lds_v = [&](int S) -> uint8_t* { return ring + NSTAGE4 * KXTILE + S * KTILE; };
+  auto lds_v = [&](int S) -> uint8_t* { return ring + 2 * KXTILE + S * KTILE; };
   const uint32_t ring_lds = lds_addr(ring);
   const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -819,7 +814,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
   };
   auto ring_v = [&](int t, int S) {
     const uint8_t* tp = vbase + (size_t)t * KTILE;
-    const uint32_t dst = ring_lds + NSTAGE4 * KXTILE + (uint32_t)S * KTILE + wave_u * 2048u;
+    const uint32_t dst = ring_lds + 2 * KXTILE + (uint32_t)S * KTILE + wave_u * 2048u;
 #pragma unroll
     for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], dst + i * 1024);
   };
@@ -850,71 +845,47 @@ __global__ __launch_bounds__(256, 1) void attn_fp4_kernel(
   for (int i = 0; i < 4; ++i) o[i] = v16f{};
   float m = -INFINITY, l = 0.f;
 
-  // K-tile exponent of the step whose softmax runs next, loaded before each
-  // barrier wait (as the FP8 kernel's K scale)
-  int ken = kebase[0];
-
-  // prologue: K(0..2) and V(0) in flight; V(-1) (stage 2) is zero.  The Q
-  // operand loads complete first, so that from here on the only vector-memory
-  // loads in flight are ring copies.
+  // Prologue: K(0), K(1), V(0) land (after the Q loads, so that from here on
+  // the only vector-memory loads in flight are ring copies), then the scores
+  // of step 0; the second barrier lets step 0 refill K stage 0.
   const int Tm1 = T - 1;
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
   ring_k(0, 0);
   ring_k(min(1, Tm1), 1);
-  ring_k(min(2, Tm1), 2);
   ring_v(0, 0);
-  *(u32x4*)(lds_v(2) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
-  *(u32x4*)(lds_v(2) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
-  // K(0), K(1) landed (at most K(2) and V(0) outstanding)
-  ring_barrier_wait10();
-  v16f sa[2], sb[2];
-  scores(lds_k(0), sa);
-  v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  float alpha_prev = 1.f;
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  asm volatile("s_barrier" ::: "memory");
+  v16f s[2];
+  scores(lds_k(0), s);
+  int ken = kebase[0];
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  asm volatile("s_barrier" ::: "memory");
 
-  // steps 0 .. T-2 (full); S = t % 3 is the stage of K(t) and V(t)
-  auto step = [&](int t, int S, v16f* s_cur, v16f* s_next) {
-    const int S1 = S == 2 ? 0 : S + 1, S2 = S == 0 ? 2 : S - 1;
-    rescale_o(o, alpha_prev);
-    ring_k(min(t + 3, Tm1), S);
-    ring_v(min(t + 1, Tm1), S1);
-    scores(lds_k(S1), s_next);
-    value_mfma(o, pb_prev, lds_v(S2), voff0, voff1);
-    pb_prev = softmax_step<true>(s_cur, ldexpf(cq, ken), m, l, alpha_prev, t * KSTEP, N, g);
-#pragma unroll
-    for (int i = 0; i < 52; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);   // VALU
+  // Step t (S = t & 1): issue K(t+2) into K stage S (K(t) was read in step
+  // t-1) and V(t+1) into V stage S^1 (V(t-1) was read in step t-1); softmax of
+  // S(t); O = alpha O + V(t) P(t); scores S(t+1) from K stage S^1.  The
+  // copies have the whole step to land: at its end every copy is waited for,
+  // and the barrier hands the stages over.  One scores buffer: the two waves
+  // of a SIMD (two workgroups per CU) overlap one's softmax with the other's
+  // MFMAs.
+  for (int t = 0; t < T; ++t) {
+    const int S = t & 1;
+    if (t + 1 < T) {
+      ring_k(min(t + 2, Tm1), S);
+      ring_v(t + 1, S ^ 1);
     }
-    ken = kebase[t + 1];
-    ring_barrier_wait10();
-  };
-  int t = 0, S = 0;
-  for (; t + 2 < T; t += 2) {
-    step(t, S, sa, sb);
-    S = S == 2 ? 0 : S + 1;
-    step(t + 1, S, sb, sa);
-    S = S == 2 ? 0 : S + 1;
-  }
-  // the last step T-1 (possibly short); V(T-1) is in stage (T-1) % 3
-  auto last = [&](int tl, int St, v16f* s_cur) {
-    const int S2 = St == 0 ? 2 : St - 1;
-    rescale_o(o, alpha_prev);
-    value_mfma(o, pb_prev, lds_v(S2), voff0, voff1);
     float alpha;
     const float c = ldexpf(cq, ken);
-    const v8i pb = (tl + 1) * KSTEP <= N ? softmax_step<true>(s_cur, c, m, l, alpha, tl * KSTEP, N, g)
-                                         : softmax_step<false>(s_cur, c, m, l, alpha, tl * KSTEP, N, g);
-    __builtin_amdgcn_s_waitcnt(0x0070);   // every ring copy has landed
-    asm volatile("s_barrier" ::: "memory");
+    const v8i pb = (t + 1) * KSTEP <= N ? softmax_step<true>(s, c, m, l, alpha, t * KSTEP, N, g)
+                                        : softmax_step<false>(s, c, m, l, alpha, t * KSTEP, N, g);
     rescale_o(o, alpha);
-    value_mfma(o, pb, lds_v(St), voff0, voff1);
-  };
-  if (t + 1 < T) {
-    step(t, S, sa, sb);
-    last(t + 1, S == 2 ? 0 : S + 1, sb);
-  } else {
-    last(t, S, sa);
+    value_mfma(o, pb, lds_v(S), voff0, voff1);
+    if (t + 1 < T) {
+      scores(lds_k(S ^ 1), s);
+      ken = kebase[t + 1];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // this step's copies landed, LDS reads done
+    asm volatile("s_barrier" ::: "memory");
   }
 
   const int q = q0 + r;
@@ -937,7 +908,7 @@ static int device_cus() {
 
 void launch_attention(const LaunchArgs& a, hipStream_t s) {
   const int BH = a.batch * a.heads;
-  const int slots = 2 * device_cus();   // two workgroups of the FP8 and MXFP4 kernels per CU
+  const int slots = 2 * device_cus();   // two workgroups of each attention kernel per CU
   const int tiles = a.n_pad / QT;
   const float tl = a.softmax_scale * LOG2E;
   if (a.mx) {
@@ -950,7 +921,7 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
     attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded,
                                                 (const int*)(a.k_expanded + (size_t)BH * ktiles * KXTILE),
                                                 a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl,
-                                                tiles);
+                                                tiles, slots);
   } else {
     auto kern = a.fuse_q ? attn_fp8_kernel<true> : attn_fp8_kernel<false>;
     kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_codes, a.k_scales,
