@@ -41,11 +41,13 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, heads: int):
+def cpu_baseline(w, heads: int, got_bits):
     """The oracle, single process with single-threaded BLAS, on the first
     ``heads`` (b, h) pairs of batch 0 of the workload: quantize of each head
-    and every query row against every key.  Returns the record and the
-    oracle's outputs [heads, N, 128] (fp64 values of bf16)."""
+    and every query row against every key, timed.  Then, untimed, the error of
+    the GPU output on those heads (``got_bits``, bf16 bits [heads, N, 128])
+    against the oracle's output and against exact attention.  Returns the
+    baseline record and the accuracy record."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -65,13 +67,14 @@ def cpu_baseline(w, heads: int):
     rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
            "sample": f"{heads} of the {w.batch * w.heads} (b,h) pairs of {w.name}, all {w.seq_len} query rows "
                      f"(quantize + attention), {dt:.1f} s wall, single-threaded NumPy"}
-    return rec, outs, (qb, kb, vb)
+    return rec, accuracy(w, got_bits, outs, (qb, kb, vb))
 
 
 def accuracy(w, got_bits, want, inputs, rows_per_head: int = 256):
-    """Error of the GPU output (bf16 bits [heads, N, 128] of batch 0) against
-    the oracle's output on the same heads, and against exact fp64 softmax
-    attention of the unquantized inputs on sampled rows."""
+    """Part of the CPU-baseline leg: error of the GPU output (bf16 bits
+    [heads, N, 128] of batch 0) against the oracle's output on the same
+    heads, and against exact fp64 softmax attention of the unquantized inputs
+    on sampled rows."""
     import numpy as np
 
     import oracle
@@ -202,8 +205,7 @@ def main():
     if not args.no_cpu_baseline:
         heads = min(args.cpu_heads, w.heads)
         got_bits = out[0, :heads].contiguous().view(torch.int16).cpu().numpy().view("uint16")
-        rec["cpu_baseline"], want, inputs = cpu_baseline(w, heads)
-        rec["accuracy"] = accuracy(w, got_bits, want, inputs)
+        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline(w, heads, got_bits)
     print(json.dumps(rec), flush=True)
 
 
