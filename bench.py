@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="kontext1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the other FLUX shapes of the metric (N = 4608 and 16896, FP8)")
     ap.add_argument("--cpu-heads", type=int, default=8, help="(b,h) pairs of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling HBM byte counters)")
@@ -95,6 +97,33 @@ def accuracy(w, got_bits, want, inputs, rows_per_head: int = 256):
             "vs_exact_fp64": {"max_abs": float(e.max()), "mean_abs": float(e.mean()),
                               "sample": f"{want.shape[0]} heads x {min(rows_per_head, w.seq_len)} rows"},
             "tolerance_vs_oracle": {"max_abs": 1e-2, "mean_abs": 1e-3}}
+
+
+def time_forward(w, steps: int, warmup: int):
+    """ms per qsdpa_forward call of workload ``w`` (inputs resident in HBM),
+    timed with HIP events on the current stream."""
+    import torch
+
+    import precision_attention_qsdpa_amd as qs
+    from workloads import TAU, draw
+
+    qb, kb, vb = draw(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).view(torch.bfloat16).to(dev) for x in (qb, kb, vb))
+    params = qs.make_params(w.batch, w.heads, w.seq_len, fmt=w.fmt, block_q=w.block_q, block_k=w.block_k,
+                            softmax_scale=TAU)
+    ws = qs.empty_workspace(params, dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        qs.qsdpa_forward(q, k, v, out=out, workspace=ws, params=params, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        qs.qsdpa_forward(q, k, v, out=out, workspace=ws, params=params, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    return e0.elapsed_time(e1) / steps
 
 
 def main():
@@ -202,6 +231,17 @@ def main():
                      "hbm_peak_GB_s": HBM_PEAK_GBS},
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_shapes and w.name == "kontext1024":
+        # the metric's other FLUX shapes (FP8): one line each, not the headline value
+        rec["shapes"] = []
+        for name in ("dev1024", "gen2048_fp8"):
+            ws_ = WORKLOADS[name]
+            ms = time_forward(ws_, steps=30, warmup=10)
+            tf = ws_.flops / (ms * 1e-3) / 1e12
+            rec["shapes"].append({"workload": name, "batch": ws_.batch, "heads": ws_.heads,
+                                  "seq_len": ws_.seq_len, "qk_format": ws_.fmt, "ms_per_step": round(ms, 4),
+                                  "value": round(tf, 2), "unit": "TFLOP/s",
+                                  "pct_fp8_peak": round(100.0 * tf / FP8_PEAK_TFLOPS, 2)})
     if not args.no_cpu_baseline:
         heads = min(args.cpu_heads, w.heads)
         got_bits = out[0, :heads].contiguous().view(torch.int16).cpu().numpy().view("uint16")
