@@ -78,10 +78,10 @@ typedef struct qsdpa_params {
   int32_t heads;         /* H >= 1 */
   int32_t seq_len;       /* N >= 1 (any value: tails are handled) */
   int32_t head_dim;      /* must be 128 */
-  int32_t block_q;       /* FP8 mode: Q tokens per scale, 64 or 128 (ignored in FP4 mode) */
-  int32_t block_k;       /* FP8 mode: K tokens per scale, must be 64 (ignored in FP4 mode) */
-  int32_t qk_format;     /* QSDPA_QK_FP8_E4M3 or QSDPA_QK_FP4_E2M1 */
-  int32_t fp4_group;     /* FP4 mode: channels per scale, must be 16 (ignored in FP8 mode) */
+  int32_t block_q;       /* FP8 mode: Q tokens per scale, 64 or 128 (ignored in the FP4 modes) */
+  int32_t block_k;       /* FP8 mode: K tokens per scale, must be 64 (ignored in the FP4 modes) */
+  int32_t qk_format;     /* QSDPA_QK_FP8_E4M3, QSDPA_QK_FP4_E2M1 or QSDPA_QK_MXFP4_E2M1 */
+  int32_t fp4_group;     /* FP4 mode: channels per scale, must be 16 (ignored otherwise) */
   float softmax_scale;   /* tau > 0 and finite, normally 1/sqrt(128) */
 } qsdpa_params;
 
