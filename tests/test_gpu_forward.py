@@ -205,3 +205,44 @@ def test_power_of_two_input_scaling(gpu_lib, fmt, shift):
     assert np.array_equal(got, ref)
     compare(got, qs_, ks_, vb, fmt, 128, [(0, 0), (0, 1)], lambda b, h: np.arange(N),
             f"scaled-{fmt}-{shift}")
+
+
+def test_forward_full_size_block_q_64(gpu_lib):
+    """The Kontext workload with 64-token Q scale blocks: in qsdpa_forward each
+    block is one wave pair of a workgroup, quantized in the attention
+    prologue."""
+    w = WORKLOADS["kontext1024"]
+    qb, kb, vb = draw(w)
+    params = qs.make_params(w.batch, w.heads, w.seq_len, fmt="fp8", block_q=64)
+    print(f"[forward] start kontext1024 block_q=64", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    rng = np.random.default_rng(64)
+    compare(out, qb, kb, vb, "fp8", 64, [(0, 5), (0, 23)], lambda b, h: sample_rows(w.seq_len, rng),
+            "kontext1024-bq64")
+
+
+def test_concurrent_streams_match_serial(gpu_lib):
+    """Two forwards on two streams at once (own inputs, outputs and
+    workspaces) give the serial results bit for bit: the library keeps no
+    state between calls."""
+    shapes = [("fp8", 1500, 3), ("mxfp4", 2100, 2)]
+    inputs, serial = [], []
+    for fmt, N, H in shapes:
+        qb, kb, vb = draw(WORKLOADS["tiny"], heads=H, seq_len=N, seed=N)
+        params = qs.make_params(1, H, N, fmt=fmt, block_q=128)
+        inputs.append((to_dev(qb), to_dev(kb), to_dev(vb), params))
+        serial.append(run_forward(qb, kb, vb, params))
+    print("[forward] two streams", flush=True)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for (q, k, v, params), s in zip(inputs, streams):
+            with torch.cuda.stream(s):
+                ws = qs.empty_workspace(params)
+                o = torch.empty_like(q)
+                qs.qsdpa_forward(q, k, v, out=o, workspace=ws, params=params, stream=s)
+                outs.append((o, ws))
+    torch.cuda.synchronize()
+    for i, (o, _) in enumerate(outs):
+        assert np.array_equal(from_dev(o), serial[i % 2]), f"stream result {i} differs"
