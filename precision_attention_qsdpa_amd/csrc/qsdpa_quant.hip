@@ -1,7 +1,9 @@
 // Statistics and quantize kernels: channel mean of K and max |V| (fp64 /
-// fp32), K smoothing, per-block FP8 / per-16-channel FP4 codes of Q and K,
-// per-channel FP8 codes of V written as key-tiles in the order the attention
-// kernel's value product consumes them.
+// fp32), K smoothing, per-block FP8, per-16-channel FP4 or per-32-channel
+// MXFP4 (E8M0 scale) codes of Q and K, per-channel FP8 codes of V written as
+// key-tiles in the order the attention kernel's value product consumes them,
+// and in FP4 mode K expanded once per head into the attention kernel's f16
+// hi/lo tiles.
 //
 // All of these kernels are bound by HBM traffic; they read bf16 rows with
 // 16-byte loads, 16 threads per 256-byte token row.
