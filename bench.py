@@ -130,7 +130,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by (batch, head) with no exchange, see DESIGN.md", file=sys.stderr)
+              "the path shards by (batch, head) with no exchange: each GPU would run this same "
+              "kernel on its share of the heads", file=sys.stderr)
         sys.exit(2)
     import torch
 
