@@ -129,7 +129,7 @@ def time_forward(w, steps: int, warmup: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by (batch, head) with no exchange: each GPU would run this same "
               "kernel on its share of the heads", file=sys.stderr)
         sys.exit(2)
