@@ -113,6 +113,24 @@ def test_zero_queries_closed_form(gpu_lib, fmt):
     assert np.max(np.abs(got - want[None, :])) <= 2.0 ** -8 * np.abs(want).max()
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+def test_identical_keys_closed_form(gpu_lib, fmt):
+    """Every key the same token: K - mu is exactly 0, so every K code and
+    scale is 0, every score is 0 and O is the mean of the dequantized V codes
+    for any Q (smoothing removes the shared key)."""
+    N = 777
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=1, seq_len=N, seed=12)
+    kb = np.broadcast_to(kb[:, :, 5:6], kb.shape).copy()
+    params = qs.make_params(1, 1, N, fmt=fmt)
+    out = run_forward(qb, kb, vb, params)
+    z = oracle.quantize(qb, kb, vb, fmt=fmt)
+    assert not np.any(z.k_codes) and not np.any(z.k_scales)
+    mean_v = oracle.decode(z.v_codes[0, 0], oracle.E4M3).mean(axis=0) * z.v_scales[0, 0].astype(np.float64)
+    want = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(mean_v))
+    got = oracle.bf16_bits_to_f64(out[0, 0])
+    assert np.max(np.abs(got - want[None, :])) <= 2.0 ** -8 * np.abs(want).max()
+
+
 def test_constant_values_stay_constant(gpu_lib):
     """V = c per channel: O/c = sum(P)/(448 l) within the E4M3 weight bound."""
     N = 2000
