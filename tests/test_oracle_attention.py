@@ -80,6 +80,17 @@ def test_worked_example_step_size_changes_codes():
     assert acc2[0, 0] == 60 + 448 * 3 and abs(l2[0] - (1 + e2)) < 1e-15
 
 
+def test_worked_example_running_max_is_kept():
+    """S = [2, 0] in one-key steps: the second step's own maximum (0) is below
+    the running one (2), so its weight is coded relative to 2: E4M3(448 e^-2)
+    = 60, not 448; l = 1 + e^-2."""
+    S = np.array([[2.0, 0.0]])
+    V = np.array([[1.0], [3.0]])
+    e2 = math.exp(-2.0)
+    acc, l, _ = oracle.online_softmax_av(S, V, step=1)
+    assert acc[0, 0] == 448 + 60 * 3 and abs(l[0] - (1 + e2)) < 1e-15
+
+
 def _tiny_inputs(N, seed=13, H=1):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((1, H, N, 128)).astype(np.float32)

@@ -56,6 +56,23 @@ def test_fp8_block_scales_by_construction():
     assert np.all(err[~normal] <= (2.0 ** -10 + 1e-7) * np.broadcast_to(s_tok, x.shape)[~normal])
 
 
+def test_q_and_k_take_their_own_block_sizes():
+    """block_q = 128, block_k = 64 on a K whose mean is 0 (each channel
+    alternates +-a): Q has one scale per 128 tokens, K one per 64 tokens, and
+    K's two halves (a = 1, then a = 4) get scales 1/448 and 4/448."""
+    N, D = 128, 128
+    sign = np.where(np.arange(N) % 2 == 0, 1.0, -1.0)[:, None]
+    a = np.where(np.arange(N) < 64, 1.0, 4.0)[:, None]
+    k = (sign * a * np.ones((N, D)))[None, None].astype(np.float32)
+    q = np.ones((1, 1, N, D), np.float32)
+    z = oracle.quantize(_bits(q), _bits(k), _bits(q), block_q=128, block_k=64)
+    assert np.all(z.k_mean == 0)
+    assert z.q_scales.shape == (1, 1, 1) and z.q_scales[0, 0, 0] == np.float32(1.0 / 448)
+    assert z.k_scales.shape == (1, 1, 2)
+    assert z.k_scales[0, 0, 0] == np.float32(1.0 / 448) and z.k_scales[0, 0, 1] == np.float32(4.0 / 448)
+    assert np.all(np.abs(decode(z.k_codes, E4M3)) == 448)
+
+
 def test_zero_block_gives_zero_scale_and_codes():
     x = np.zeros((1, 1, 130, 128), np.float32)
     x[0, 0, 64:] = 1.0
