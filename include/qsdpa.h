@@ -19,8 +19,11 @@
  *      tokens, scale s = fp32(amax/448), code = E4M3(fp32(x * fp32(448/amax)));
  *      FP4 mode: per token and 16 consecutive channels, s = fp32(amax/6),
  *      code = E2M1(fp32(x * fp32(6/amax))); an all-zero block has s = 0 and
- *      zero codes.  E4M3/E2M1 round to nearest even and saturate;
- *   4. V per channel: sV = fp32(vmax/448), code = E4M3(fp32(V * fp32(448/vmax)));
+ *      zero codes, and so does a block whose inverse fp32(F/amax) overflows
+ *      (0 < amax < F/FLT_MAX: below about 1.3e-36 for FP8, 1.8e-38 for FP4).
+ *      E4M3/E2M1 round to nearest even and saturate;
+ *   4. V per channel: sV = fp32(vmax/448), code = E4M3(fp32(V * fp32(448/vmax)))
+ *      (zero scale and codes for a channel as in 3);
  *   5. scores S = tau * dequant(Q) . dequant(K);
  *   6. online softmax over steps of 64 keys in ascending order:
  *      m = running max, p = exp(S - m), P = E4M3(448 p) fed to an FP8 P.V

@@ -34,6 +34,9 @@ head dimension D = 128, queries i and keys j:
    a = max |x|: if a == 0 the scale and all codes are 0; otherwise
    inv = fp32(F / a), s = fp32(a / F), code = E(fp32(x * inv)) with F = 448,
    E = E4M3 (FP8) or F = 6, E = E2M1 (FP4).  The value of a code is code * s.
+   A block whose fp32 inverse F / a overflows (0 < a < F / FLT_MAX, values
+   below about 1.3e-36 for FP8 and 1.8e-38 for FP4) has no fp32 inverse scale
+   and is coded as an all-zero block too.
 4. V codes (FP8 in both modes, since attention stays FP8).  Per channel d:
    inv = fp32(448 / vmax[d]), sV[d] = fp32(vmax[d] / 448),
    code = E4M3(fp32(V * inv)); zero rule as in 3.
@@ -105,15 +108,26 @@ def smooth_k(k: np.ndarray, mu: np.ndarray) -> np.ndarray:
     return k.astype(np.float32) - mu[:, :, None, :]
 
 
+def _live(amax: np.ndarray, fmax: float) -> np.ndarray:
+    """Blocks that get codes: those whose inverse scale fp32(F / amax) is
+    finite.  That excludes amax = 0, and also 0 < amax < F / FLT_MAX (about
+    1.3e-36 for F = 448, 1.8e-38 for F = 6), where the fp32 inverse overflows:
+    such a block is coded like an all-zero block (scale 0, codes 0)."""
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = np.float32(fmax) / np.asarray(amax, dtype=np.float32)
+    return np.isfinite(inv) & (np.asarray(amax) > 0)
+
+
 def _codes_from(x32: np.ndarray, amax: np.ndarray, fmax: float, fmt):
-    """Scales and codes of fp32 values ``x32`` given each element's block
-    maximum ``amax`` (broadcast to x32's shape)."""
+    """Codes of fp32 values ``x32`` given each element's block maximum
+    ``amax`` (broadcast to x32's shape)."""
     fmax32 = np.float32(fmax)
-    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    live = _live(amax, fmax)
+    safe = np.where(live, amax, np.float32(1.0)).astype(np.float32)
     inv = (fmax32 / safe).astype(np.float32)
     scaled = (x32 * inv).astype(np.float32)
     vals = round_to(scaled.astype(np.float64), fmt)
-    vals = np.where(amax > 0, vals, 0.0)
+    vals = np.where(live, vals, 0.0)
     return encode(vals, fmt)
 
 
@@ -125,7 +139,7 @@ def quantize_fp8_blocks(x32: np.ndarray, block: int):
     amax_blk = np.zeros((B, H, nblk), dtype=np.float32)
     for t in range(nblk):
         amax_blk[:, :, t] = np.abs(x32[:, :, t * block:(t + 1) * block, :]).max(axis=(2, 3))
-    scales = np.where(amax_blk > 0, amax_blk / np.float32(448.0), np.float32(0.0)).astype(np.float32)
+    scales = np.where(_live(amax_blk, 448.0), amax_blk / np.float32(448.0), np.float32(0.0)).astype(np.float32)
     amax_tok = np.repeat(amax_blk, block, axis=2)[:, :, :N, None]
     codes = _codes_from(x32, np.broadcast_to(amax_tok, x32.shape), 448.0, E4M3)
     return codes, scales
@@ -138,7 +152,7 @@ def quantize_fp4_groups(x32: np.ndarray, group: int = FP4_GROUP):
     B, H, N, D = x32.shape
     g = x32.reshape(B, H, N, D // group, group)
     amax = np.abs(g).max(axis=4)
-    scales = np.where(amax > 0, amax / np.float32(6.0), np.float32(0.0)).astype(np.float32)
+    scales = np.where(_live(amax, 6.0), amax / np.float32(6.0), np.float32(0.0)).astype(np.float32)
     codes = _codes_from(g, np.broadcast_to(amax[..., None], g.shape), 6.0, E2M1).reshape(B, H, N, D)
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
     return packed, scales
@@ -176,7 +190,7 @@ def quantize_v(v: np.ndarray, vmax: np.ndarray):
     """Per-channel FP8 codes of V.  v float64 [B,H,N,D] holding bf16 values,
     vmax fp32 [B,H,D] -> (codes uint8 [B,H,N,D], scales fp32 [B,H,D])."""
     v32 = v.astype(np.float32)
-    scales = np.where(vmax > 0, vmax / np.float32(448.0), np.float32(0.0)).astype(np.float32)
+    scales = np.where(_live(vmax, 448.0), vmax / np.float32(448.0), np.float32(0.0)).astype(np.float32)
     amax = np.broadcast_to(vmax[:, :, None, :], v32.shape)
     return _codes_from(v32, amax, 448.0, E4M3), scales
 

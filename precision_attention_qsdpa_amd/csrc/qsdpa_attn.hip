@@ -316,8 +316,10 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
       __syncthreads();
       amax = block_q == 128 ? fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3]))
                             : fmaxf(qred[wave & 2], qred[(wave & 2) + 1]);
-      const float inv = amax > 0.f ? FP8_MAX / amax : 0.f;
-      qscale = amax > 0.f ? amax / FP8_MAX : 0.f;
+      const float inv0 = FP8_MAX / amax;   // not finite: amax = 0 or below FP8_MAX / FLT_MAX
+      const bool live = inv0 < INFINITY;
+      const float inv = live ? inv0 : 0.f;
+      qscale = live ? amax / FP8_MAX : 0.f;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(128) void stats_final_kernel(
   }
   mu[bh * D + d] = (float)(t / (double)N);
   vamax[bh * D + d] = mm;
-  vscale[bh * D + d] = mm > 0.f ? mm / FP8_MAX : 0.f;
+  vscale[bh * D + d] = FP8_MAX / mm < INFINITY ? mm / FP8_MAX : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -130,13 +130,16 @@ __device__ __forceinline__ void fp8_block(const uint16_t* __restrict__ x, const 
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = amax > 0.f ? FP8_MAX / amax : 0.f;
-  if (tid == 0) scales[blk] = amax > 0.f ? amax / FP8_MAX : 0.f;
+  // the block gets codes when its fp32 inverse scale is finite: not for
+  // amax = 0, nor for amax below FP8_MAX / FLT_MAX, where it overflows
+  const float inv = FP8_MAX / amax;
+  const bool live = inv < INFINITY;
+  if (tid == 0) scales[blk] = live ? amax / FP8_MAX : 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int n = n0 + rl + 16 * i;
     u32x2 out = {0u, 0u};
-    if (amax > 0.f && n < N) {
+    if (live && n < N) {
       int lo = cvt_e4m3x2<false>(clamp448(val[i][0] * inv), clamp448(val[i][1] * inv), 0);
       lo = cvt_e4m3x2<true>(clamp448(val[i][2] * inv), clamp448(val[i][3] * inv), lo);
       int hi = cvt_e4m3x2<false>(clamp448(val[i][4] * inv), clamp448(val[i][5] * inv), 0);
@@ -185,8 +188,8 @@ __global__ __launch_bounds__(256) void quant_qk_fp4_kernel(
   }
   u32x2 out = {0u, 0u};
   float scale = 0.f;
-  if (amax > 0.f) {
-    const float inv = FP4_MAX / amax;
+  const float inv = FP4_MAX / amax;   // +inf for amax = 0 or below FP4_MAX / FLT_MAX: zero codes
+  if (inv < INFINITY) {
     scale = amax / FP4_MAX;
     out[0] = e2m1_word8(val, inv);
     out[1] = e2m1_word8(val + 8, inv);
@@ -213,7 +216,8 @@ __device__ __forceinline__ int vtile_pos(int key) {
 // channel row (keys 4m..4m+3 map to bytes p..p+3), so each thread writes one
 // 32-bit word per channel.  The LDS copy of the tile uses 72-byte rows, which
 // keeps those word writes free of bank conflicts; it is then copied out as the
-// 8 KB tile.  Keys at or past N and channels with vmax = 0 get zero codes.
+// 8 KB tile.  Keys at or past N and channels with no finite inverse scale
+// (vmax = 0, or below FP8_MAX / FLT_MAX) get zero codes.
 constexpr int VROW = 72;
 
 __device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, const float* __restrict__ vamax,
@@ -225,8 +229,9 @@ __device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, con
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float a = vamax[bh * D + cg * 8 + j];
-    nz[j] = a > 0.f;
-    inv[j] = nz[j] ? FP8_MAX / a : 0.f;
+    inv[j] = FP8_MAX / a;   // +inf for a = 0 or below FP8_MAX / FLT_MAX: zero codes
+    nz[j] = inv[j] < INFINITY;
+    inv[j] = nz[j] ? inv[j] : 0.f;
   }
   float val[4][8];
 #pragma unroll

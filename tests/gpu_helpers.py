@@ -96,3 +96,39 @@ def run_forward(q_bits, k_bits, v_bits, params):
     out = qs.qsdpa_forward(q, k, v, params=params)
     torch.cuda.synchronize()
     return from_dev(out)
+
+
+def tiny_magnitude_inputs(N: int = 300, seed: int = 31):
+    """bf16 bit patterns of Q, K, V [1, 2, N, 128] (N even, N >= 216) with
+    token bands and V channels whose magnitudes sit around the limit below
+    which an inverse scale F / amax overflows fp32 (F / FLT_MAX is about
+    1.3e-36 for F = 448 and 1.8e-38 for F = 6): tokens 64..127 near 1e-37,
+    128..191 near 7e-37, 192..207 bf16 subnormals near 4e-39, 208..215 deep
+    subnormals that are mostly 0; every 7th value of those bands exactly 0;
+    V channels 3, 4, 5 near 1e-37, 7e-37 and 4e-39, channel 6 all 0; the rest
+    N(0, 1).  K is made of pairs of opposite tokens, so its channel mean is
+    exactly 0 and smoothing leaves it unchanged."""
+    from workloads import to_bf16_bits
+
+    rng = np.random.default_rng(seed)
+    band = np.ones(N, np.float32)
+    band[64:128], band[128:192], band[192:208], band[208:216] = 1e-37, 2e-36 / 3, 4e-39, 1e-41
+    holes = np.ones(128, np.float32)
+    holes[::7] = 0
+
+    def shaped(x):
+        x = x * band[None, None, :, None]
+        x[:, :, 64:216] *= holes
+        return x
+
+    q = shaped(rng.standard_normal((1, 2, N, 128)).astype(np.float32))
+    half = rng.standard_normal((1, 2, N // 2, 128)).astype(np.float32)
+    k = np.empty((1, 2, N, 128), np.float32)
+    k[:, :, 0::2], k[:, :, 1::2] = half, -half
+    k = shaped(k)
+    v = rng.standard_normal((1, 2, N, 128)).astype(np.float32)
+    v[..., 3] *= np.float32(1e-37)
+    v[..., 4] *= np.float32(2e-36 / 3)
+    v[..., 5] *= np.float32(4e-39)
+    v[..., 6] = 0
+    return to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import precision_attention_qsdpa_amd as qs
-from gpu_helpers import from_dev, run_forward, to_dev
+from gpu_helpers import from_dev, run_forward, tiny_magnitude_inputs, to_dev
 from workloads import TAU, WORKLOADS, draw
 
 pytestmark = pytest.mark.gpu
@@ -129,6 +129,20 @@ def test_identical_keys_closed_form(gpu_lib, fmt):
     want = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(mean_v))
     got = oracle.bf16_bits_to_f64(out[0, 0])
     assert np.max(np.abs(got - want[None, :])) <= 2.0 ** -8 * np.abs(want).max()
+
+
+@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128), ("mxfp4", 128)])
+def test_forward_tiny_magnitudes(gpu_lib, fmt, bq):
+    """Tokens and V channels near and below the fp32 overflow limit of their
+    inverse scales, bf16 subnormals and zeros among them: the output is finite
+    and within the tolerance of the oracle."""
+    qb, kb, vb = tiny_magnitude_inputs()
+    N = qb.shape[2]
+    params = qs.make_params(1, 2, N, fmt=fmt, block_q=bq)
+    print(f"[forward] tiny magnitudes fmt={fmt} bq={bq}", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    assert np.all(np.isfinite(oracle.bf16_bits_to_f64(out)))
+    compare(out, qb, kb, vb, fmt, bq, [(0, 0), (0, 1)], lambda b, h: np.arange(N), f"tiny-{fmt}-bq{bq}")
 
 
 def test_constant_values_stay_constant(gpu_lib):

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import precision_attention_qsdpa_amd as qs
-from gpu_helpers import read_workspace, run_quantize
+from gpu_helpers import read_workspace, run_quantize, tiny_magnitude_inputs
 from workloads import WORKLOADS, draw
 
 pytestmark = pytest.mark.gpu
@@ -86,6 +86,20 @@ def test_quantize_zero_blocks(gpu_lib):
     vb[:, :, :, 5] = 0
     for fmt in ("fp8", "fp4", "mxfp4"):
         check_quantize(qb, kb, vb, fmt, 64, [(0, 0), (0, 1)], f"zero-{fmt}")
+
+
+@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128), ("mxfp4", 128)])
+def test_quantize_tiny_magnitudes(gpu_lib, fmt, bq):
+    """Blocks and V channels below the fp32 overflow limit of their inverse
+    scale get zero scales and codes (no 0 * inf), blocks just above it keep
+    full-range codes with subnormal scales, and bf16 subnormals are coded as
+    the oracle codes them."""
+    qb, kb, vb = tiny_magnitude_inputs()
+    z = oracle.quantize(qb[:, :1], kb[:, :1], vb[:, :1], fmt=fmt, block_q=bq, block_k=64)
+    assert np.all(z.k_mean == 0) and z.v_scales[0, 0, 3] == 0 and z.v_scales[0, 0, 4] > 0
+    if fmt == "fp8" and bq == 64:
+        assert z.q_scales[0, 0, 1] == 0 and z.k_scales[0, 0, 1] == 0 and 0 < z.q_scales[0, 0, 2] < 2.0 ** -126
+    check_quantize(qb, kb, vb, fmt, bq, [(0, 0), (0, 1)], f"tiny-{fmt}-bq{bq}")
 
 
 def e2m1_tie_rows(rng, n_rows):

@@ -81,6 +81,38 @@ def test_zero_block_gives_zero_scale_and_codes():
     assert scales[0, 0, 1] == np.float32(1.0 / 448) and np.all(codes[0, 0, 64:] == 0x7E)
 
 
+def test_blocks_without_an_fp32_inverse_scale_are_zero_blocks():
+    """F / amax overflows fp32 when amax < F / FLT_MAX (about 1.3e-36 for
+    F = 448 and 1.8e-38 for F = 6).  Such a block has no fp32 inverse scale:
+    scale 0 and zero codes, with no NaN from 0 * inf.  A block just above the
+    limit keeps full-range codes (+-448, +-6) and its subnormal fp32 scale."""
+    flt_max = float(np.finfo(np.float32).max)
+    assert 1e-37 < 448 / flt_max < 2e-36 and 1.5e-38 < 6 / flt_max < 2e-38
+    pattern = np.where(np.arange(128) % 3 == 0, 0.0, np.where(np.arange(128) % 2 == 0, 1.0, -0.5))
+    pattern[1] = -1.0
+    x = np.zeros((1, 1, 192, 128), np.float32)
+    x[0, 0, :64] = np.float32(1e-37) * pattern
+    x[0, 0, 64:128] = np.float32(2e-36) * pattern
+    x[0, 0, 128:] = pattern
+    codes, scales = oracle.quantize_fp8_blocks(x, 64)
+    assert scales[0, 0, 0] == 0 and np.all(codes[0, 0, :64] == 0)
+    assert scales[0, 0, 1] == np.float32(np.float32(2e-36) / np.float32(448)) and scales[0, 0, 1] < 2.0 ** -126
+    vals = decode(codes[0, 0, 64:128], E4M3)
+    assert np.max(vals) == 448 and np.min(vals) == -448 and np.all(vals[:, pattern == 0] == 0)
+    assert scales[0, 0, 2] == np.float32(1 / 448)
+    g = np.zeros((1, 1, 1, 128), np.float32)
+    g[0, 0, 0, :16] = np.float32(1.5e-38) * pattern[:16]
+    g[0, 0, 0, 16:32] = np.float32(2e-38) * pattern[:16]
+    packed, fscales = oracle.quantize_fp4_groups(g)
+    assert fscales[0, 0, 0, 0] == 0 and np.all(packed[0, 0, 0, :8] == 0)
+    assert fscales[0, 0, 0, 1] > 0 and np.max(np.abs(decode(oracle.unpack_fp4(packed)[0, 0, 0, 16:32], E2M1))) == 6
+    v = np.zeros((1, 1, 4, 128))
+    v[0, 0, :, 0], v[0, 0, :, 1] = 1e-37, 2e-36
+    vcodes, vscales = oracle.quantize_v(v, np.abs(v).max(axis=2).astype(np.float32))
+    assert vscales[0, 0, 0] == 0 and np.all(vcodes[0, 0, :, 0] == 0)
+    assert vscales[0, 0, 1] > 0 and np.all(decode(vcodes[0, 0, :, 1], E4M3) == 448)
+
+
 def test_fp4_groups_and_nibble_order():
     """One token whose first group spans the full E2M1 range (scale 1), so
     the codes are read off the format table; the even channel is the low nibble."""
