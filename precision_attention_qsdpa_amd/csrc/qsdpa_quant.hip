@@ -18,6 +18,12 @@
 
 namespace qsdpa {
 
+// The passes that re-read K and V after the statistics pass (which walks the
+// (b,h) pairs in order) take them last-first: the pairs the statistics pass
+// read last are then re-read first, while they are still in the caches
+// (2048x2048: the quantize pass 5 % faster; Kontext's K and V fit either way).
+__device__ __forceinline__ int last_first(int y) { return (int)gridDim.y - 1 - y; }
+
 // ---------------------------------------------------------------------------
 // Channel statistics, pass 1: per (b,h, token range of STATS_ROWS tokens)
 // partial fp64 sums of K and fp32 maxima of |V| over the range.
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(256) void quant_qk_fp4_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
     uint8_t* __restrict__ qc, float* __restrict__ qs, uint8_t* __restrict__ kc,
     float* __restrict__ ks, int N, int n_pad) {
-  const int bh = blockIdx.y;
+  const int bh = last_first(blockIdx.y);
   const bool is_k = blockIdx.z == 1;
   const uint16_t* x = is_k ? k : q;
   uint8_t* codes = is_k ? kc : qc;
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(
     int N, int n_pad, int first_block) {
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * VROW];
-  const int bh = blockIdx.y;
+  const int bh = last_first(blockIdx.y);
   const int qb = n_pad / BQ, kb = n_pad / KSTEP;
   const int b = blockIdx.x + first_block;   // first_block = qb: skip the Q blocks
   if (b < qb) {
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ vamax,
                                                       uint8_t* __restrict__ vc, int N, int n_pad) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * VROW];
-  quant_v_tile(v, vamax, vc, N, n_pad, blockIdx.y, blockIdx.x, tile);
+  quant_v_tile(v, vamax, vc, N, n_pad, last_first(blockIdx.y), blockIdx.x, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
     uint8_t* __restrict__ qs, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks, uint8_t* __restrict__ vc,
     int N, int n_pad, int first_block) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * VROW];
-  const int bh = blockIdx.y, nb = n_pad / KSTEP;
+  const int bh = last_first(blockIdx.y), nb = n_pad / KSTEP;
   const int b = blockIdx.x + first_block;
   if (b < nb) {
     mx_block(q, nullptr, qc, qs, false, N, n_pad, bh, b);
