@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSDPA_ABI_VERSION 3
+#define QSDPA_ABI_VERSION 4
 #define QSDPA_HEAD_DIM 128
 
 /* Status codes (return values). */
@@ -115,14 +115,19 @@ typedef struct qsdpa_params {
  *   stats:            scratch for partial channel sums (fp64) and maxima.
  *   k_expanded:       FP4 mode only (0 bytes in other modes): every K
  *                     element x = code * scale (one fp32 product) times
- *                     2^-E of its 64-key tile, split into f16 hi = f16(x')
- *                     and lo = f16(x' - hi), both rounded to nearest even,
- *                     as f16 [BH][n_pad/64][2][64][128]: per tile the hi
- *                     tile, then the lo tile; in a key row the 8-channel
- *                     chunk c is stored at chunk position c ^ (key & 15).
- *                     Then int32 E [BH][n_pad/64]: E = e - 138, e the
- *                     biased exponent field of the largest K scale of the
- *                     tile, so |x'| < 24576 and hi/lo never overflow f16.
+ *                     2^-E of its 64-key tile, x', as hi = f16(x') and the
+ *                     E4M3 bytes lo8 = E4M3(fp32(x' - hi) * 2^5) and
+ *                     hi8 = E4M3(hi * 2^-6), all rounded to nearest even.
+ *                     Per tile 32 KB: the hi tile f16 [64 keys][128], its
+ *                     8-channel chunk c of a key row stored at chunk
+ *                     position c ^ (key & 15); then the correction tile
+ *                     u8 [64 keys][16 chunks][16], whose chunk 2c + i holds
+ *                     lo8 (i = 0) or hi8 (i = 1) of channels 16c .. 16c + 15
+ *                     and is stored at position (2c + i) ^ (key & 15).
+ *                     [BH][n_pad/64] such tiles, then int32 E [BH][n_pad/64]:
+ *                     E = e - 138, e the biased exponent field of the
+ *                     largest K scale of the tile, so |x'| < 24576 and
+ *                     none of the three overflows.
  */
 typedef struct qsdpa_layout {
   uint64_t q_codes, q_scales, k_codes, k_scales, k_mean, v_codes, v_scales, v_amax, stats;

@@ -39,7 +39,7 @@ class QsdpaParams(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
-ABI_VERSION = 3   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
+ABI_VERSION = 4   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
 
 
 class QsdpaLayout(ctypes.Structure):

@@ -729,20 +729,27 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
 
 // ---------------------------------------------------------------------------
 // FP4 kernel: Q and K arrive as E2M1 codes with an fp32 scale per 16
-// channels.  Q is dequantized once into registers, and K comes as the f16
-// hi/lo tiles the quantize pass expanded (hi = f16(x), lo = f16(x - hi),
-// about 2^-22 relative), so the scores are three f16 MFMAs per 16-channel
-// chunk (hi.hi + lo.hi + hi.lo) and keep fp32-level accuracy while P and V
-// stay FP8.  Before the split, a query row is scaled by 2^-EQ and a K tile by
-// 2^-EK (fp4_norm_exp), which keeps every f16 in range; the softmax constant
-// tau * log2(e) * 2^(EQ + EK) of the lane and step takes both back.
+// channels.  Q is dequantized once into registers, and K comes in the tiles
+// the quantize pass expanded.  With x' = code * scale * 2^-E, hi = f16(x')
+// and lo = x' - hi (exact in fp32, at most 2^-11 |x'|), a score is
+//   sum hi_q hi_k             one f16 MFMA per 16-channel chunk (its
+//                             products are exact and it keeps 24 bits below
+//                             the largest)
+// + sum (hi_q lo_k + lo_q hi_k)   one FP8 MFMA per 32 channels, on E4M3
+//                             copies hi8 = E4M3(hi 2^-6) and lo8 = E4M3(lo 2^5)
+//                             concatenated along the contraction, its E8M0
+//                             scale 2^1 undoing the powers of two;
+// the FP8 roundings move each correction by at most 2^-4 of itself, so a
+// score is good to about 2^-15 of its terms.  Before the split, a query row
+// is scaled by 2^-EQ and a K tile by 2^-EK (fp4_norm_exp), which keeps every
+// f16 and E4M3 value in range; the softmax constant tau * log2(e) *
+// 2^(EQ + EK) of the lane and step takes both back.  P and V stay FP8.
 // The tiles reach LDS as in the FP8 kernel, by asynchronous copies
 // (global_load_lds_dwordx4), through a ring of 2 stages of 32 KB K + 8 KB V^T:
 // 80 KB, so that two workgroups share a CU and two waves share each SIMD.
-// The f16 Q operand alone takes 64 registers, so a wave has one scores
-// buffer: its softmax and its MFMAs alternate, and the other wave of the SIMD
-// fills the gaps (MFMA 72 % busy at 2048^2, against 51 % with one wave per
-// SIMD, three stages and double-buffered scores).
+// The Q operands take 64 registers, so a wave has one scores buffer: its
+// softmax and its MFMAs alternate, and the other wave of the SIMD fills the
+// gaps.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kx,
@@ -763,10 +770,15 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
   const int q0 = tile * QT + wave * QW;
   const int T = (N + KSTEP - 1) / KSTEP;
 
-  // Q operand: chunk c covers channels 16c + 8g .. 16c + 8g + 7 of query q0 + r,
-  // scaled by 2^-EQ of the query row (both lanes of the row read all 8 scales);
-  // the softmax constant of the lane takes 2^EQ back
-  v8h qhi[8], qlo[8];
+  // Q operands of query q0 + r, scaled by 2^-EQ of the query row (both lanes
+  // of the row read all 8 scales; the softmax constant of the lane takes 2^EQ
+  // back):
+  //   qhi[c]: hi of channels 16c + 8g .. 16c + 8g + 7 (f16 MFMA, chunk c);
+  //   qx8[p]: the 32 FP8 bytes hi8 (channels 16c .. 16c + 15) then lo8 (same
+  //           channels) of chunk c = 2p + g, matching the K correction chunks
+  //           lo8, hi8 of that chunk in the FP8 MFMA of channels 32p .. 32p + 31.
+  v8h qhi[8];
+  v8i qx8[4];
   float cq;
   {
     const size_t qrow = (size_t)bh * n_pad + q0 + r;
@@ -778,16 +790,34 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
     }
     const int EQ = fp4_norm_exp(smax);
     cq = ldexpf(tau_log2e, EQ);
+    auto scaled = [&](uint32_t code, float scale) {
+      float x = e2m1_value(code) * scale;
+      asm volatile("" : "+v"(x));
+      return ldexpf(x, -EQ);
+    };
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t w = *(const uint32_t*)(qc + qrow * 64 + 8 * c + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = e2m1_value((w >> (4 * e)) & 15u) * sc[c];
-        asm volatile("" : "+v"(x));
-        x = ldexpf(x, -EQ);
-        qhi[c][e] = (_Float16)x;
-        qlo[c][e] = (_Float16)(x - (float)qhi[c][e]);
+      for (int e = 0; e < 8; ++e) qhi[c][e] = (_Float16)scaled((w >> (4 * e)) & 15u, sc[c]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int c = 2 * p + g;
+      const u32x2 w = *(const u32x2*)(qc + qrow * 64 + 8 * c);
+      const float scale = qs[qrow * 8 + c];
+      float h8[16], l8[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float x = scaled((w[e >> 3] >> (4 * (e & 7))) & 15u, scale);
+        const float h = (float)(_Float16)x;
+        h8[e] = h * 0.015625f;
+        l8[e] = (x - h) * 32.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qx8[p][j] = cvt_e4m3x2<true>(h8[4 * j + 2], h8[4 * j + 3], cvt_e4m3x2<false>(h8[4 * j], h8[4 * j + 1], 0));
+        qx8[p][4 + j] = cvt_e4m3x2<true>(l8[4 * j + 2], l8[4 * j + 3], cvt_e4m3x2<false>(l8[4 * j], l8[4 * j + 1], 0));
       }
     }
   }
@@ -821,24 +851,33 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
     for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], dst + i * 1024);
   };
 
-  // scores of a 64-key tile: the chains of keys 0..31 and 32..63 interleaved
+  // scores of a 64-key tile: the chains of keys 0..31 and 32..63 interleaved;
+  // per 32 channels two f16 hi.hi MFMAs and one FP8 correction MFMA, whose
+  // lane operand is correction chunks 4p + 2g (lo8) and 4p + 2g + 1 (hi8) of
+  // its key row against qx8[p] (hi8, lo8): lo_k hi_q + hi_k lo_q, times the
+  // E8M0 scale 2^1 (byte 128) that undoes 2^5 * 2^-6
   auto scores = [&](const uint8_t* kbuf, v16f* s) {
     s[0] = v16f{};
     s[1] = v16f{};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      v8h ah[2], al[2];
+    for (int p = 0; p < 4; ++p) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        ah[kb] = *(const v8h*)(kbuf + kh_off(kb * 32 + r, 2 * c + g));
-        al[kb] = *(const v8h*)(kbuf + KXTILE / 2 + kh_off(kb * 32 + r, 2 * c + g));
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * p + h;
+        v8h ah[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ah[kb] = *(const v8h*)(kbuf + kh_off(kb * 32 + r, 2 * c + g));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[kb], qhi[c], s[kb], 0, 0, 0);
       }
+      v8i ax[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[kb], qhi[c], s[kb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb)
+        ax[kb] = lds_v8i(kbuf + KXTILE / 2 + kh_off(kb * 32 + r, 4 * p + 2 * g),
+                         kbuf + KXTILE / 2 + kh_off(kb * 32 + r, 4 * p + 2 * g + 1));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[kb], qhi[c], s[kb], 0, 0, 0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[kb], qlo[c], s[kb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ax[kb], qx8[p], s[kb], 0, 0, 0, 128, 0, 127);
     }
   };
 

@@ -390,10 +390,16 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
 // ---------------------------------------------------------------------------
 // FP4 mode: K expanded once per head for the attention kernel's score MFMAs.
 // Each element x = code * scale, times the tile's power of two 2^-E
-// (fp4_norm_exp of the tile's largest scale), becomes hi = f16(x') and
-// lo = f16(x' - hi) (both round to nearest even; hi + lo carries x' to about
-// 2^-22 relative), written as 32 KB per 64-key tile in the LDS order the
-// attention kernel reads, so that it can copy tiles into LDS unchanged; E
+// (fp4_norm_exp of the tile's largest scale), gives
+//   hi = f16(x')                      (f16 hi.hi MFMA operand)
+//   lo8 = E4M3((x' - hi) * 2^5)       (FP8 correction operands: x' - hi is
+//   hi8 = E4M3(hi * 2^-6)              exact in fp32, the powers of two keep
+//                                      both below 448)
+// all rounded to nearest even, written as 32 KB per 64-key tile in the LDS
+// order the attention kernel reads, so that it can copy tiles into LDS
+// unchanged: the 16 KB f16 hi tile, then the 16 KB correction tile whose
+// 16-byte chunk 2c + i of a key row holds lo8 (i = 0) or hi8 (i = 1) of the
+// 16 channels 16c .. 16c + 15 (both tiles with the kh_off chunk swizzle); E
 // goes to kexp[tile].  grid = (n_pad/64, BH), block = 256; a thread expands
 // 4 of the tile's 64 x 16 chunks of 8 channels.
 // ---------------------------------------------------------------------------
@@ -423,21 +429,30 @@ __global__ __launch_bounds__(256) void expand_k_fp4_kernel(const uint8_t* __rest
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = threadIdx.x + 256 * i;
-    const int key = idx >> 4, c = idx & 15;
-    v8h hv, lv;
+    const int key = idx >> 4, c8 = idx & 15;
+    v8h hv;
+    float lo[8], h8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       // x rounded to fp32 first (no fused multiply-convert), then scaled
-      // exactly, so that hi and lo are f16(x') and f16(x' - hi), signed zeros
-      // included
+      // exactly; the scalings by 2^5 and 2^-6 are exact too
       float x = e2m1_value((w[i] >> (4 * e)) & 15u) * s[i];
       asm volatile("" : "+v"(x));
       x = ldexpf(x, -E);
       hv[e] = (_Float16)x;
-      lv[e] = (_Float16)(x - (float)hv[e]);
+      lo[e] = (x - (float)hv[e]) * 32.f;
+      h8[e] = (float)hv[e] * 0.015625f;
     }
-    *(v8h*)(dst + kh_off(key, c)) = hv;
-    *(v8h*)(dst + KXTILE / 2 + kh_off(key, c)) = lv;
+    u32x2 lw, hw;
+    lw[0] = (uint32_t)cvt_e4m3x2<true>(lo[2], lo[3], cvt_e4m3x2<false>(lo[0], lo[1], 0));
+    lw[1] = (uint32_t)cvt_e4m3x2<true>(lo[6], lo[7], cvt_e4m3x2<false>(lo[4], lo[5], 0));
+    hw[0] = (uint32_t)cvt_e4m3x2<true>(h8[2], h8[3], cvt_e4m3x2<false>(h8[0], h8[1], 0));
+    hw[1] = (uint32_t)cvt_e4m3x2<true>(h8[6], h8[7], cvt_e4m3x2<false>(h8[4], h8[5], 0));
+    // 8-channel chunk c8 is half (c8 & 1) of 16-channel chunk c8 >> 1
+    const int half = (c8 & 1) * 8, c16 = c8 >> 1;
+    *(v8h*)(dst + kh_off(key, c8)) = hv;
+    *(u32x2*)(dst + KXTILE / 2 + kh_off(key, 2 * c16) + half) = lw;
+    *(u32x2*)(dst + KXTILE / 2 + kh_off(key, 2 * c16 + 1) + half) = hw;
   }
 }
 

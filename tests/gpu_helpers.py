@@ -68,16 +68,26 @@ def read_workspace(ws: torch.Tensor, params, N: int) -> dict:
     out["q_codes_pad"] = sec(L.q_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, N:]
     out["k_codes_pad"] = sec(L.k_codes, BH * L.n_pad * crb, np.uint8).reshape(B, H, L.n_pad, crb)[:, :, N:]
     if params.qk_format == qs.QSDPA_QK_FP4_E2M1:
-        # expanded K: per 64-key tile hi then lo, 8-channel chunk c of key row r at position c ^ (r & 15)
-        x = sec(L.k_expanded, BH * L.n_pad * 256, np.uint16).reshape(B, H, L.n_pad // 64, 2, 64, 16, 8)
+        # expanded K, per 64-key tile: the f16 hi tile (16 KB, 8-channel chunk c of
+        # key row r at chunk position c ^ (r & 15)), then the correction tile (16 KB,
+        # 16-byte chunk 2c + i of key row r at position (2c + i) ^ (r & 15): E4M3
+        # lo8 (i = 0) or hi8 (i = 1) of channels 16c .. 16c + 15)
+        tiles = L.n_pad // 64
+        raw_t = sec(L.k_expanded, BH * tiles * 32768, np.uint8).reshape(B, H, tiles, 2, 64, 16, 16)
         r = np.arange(64)[:, None]
         pos = np.arange(16)[None, :] ^ (r & 15)                  # [64 rows, 16 chunks] -> stored position
-        nat = np.take_along_axis(x, pos[None, None, None, None, :, :, None], axis=5)
-        nat = nat.reshape(B, H, L.n_pad // 64, 2, 64, 128).transpose(0, 1, 3, 2, 4, 5).reshape(B, H, 2, L.n_pad, 128)
-        out["k_hi"], out["k_lo"] = nat[:, :, 0, :N], nat[:, :, 1, :N]
-        out["k_hilo_pad"] = nat[:, :, :, N:]
+        nat = np.take_along_axis(raw_t, pos[None, None, None, None, :, :, None], axis=5)   # chunks in order
+        hi = np.ascontiguousarray(nat[:, :, :, 0]).view(np.uint16).reshape(B, H, tiles, 64, 128)
+        cor = nat[:, :, :, 1].reshape(B, H, tiles, 64, 8, 2, 16)                          # [.., c, i, byte]
+        lo8 = cor[..., 0, :].reshape(B, H, tiles, 64, 128)
+        hi8 = cor[..., 1, :].reshape(B, H, tiles, 64, 128)
+        flat = lambda a: a.reshape(B, H, L.n_pad, 128)
+        out["k_hi"], out["k_lo8"], out["k_hi8"] = flat(hi)[:, :, :N], flat(lo8)[:, :, :N], flat(hi8)[:, :, :N]
+        out["k_hilo_pad"] = np.concatenate([flat(hi)[:, :, N:].view(np.uint8).reshape(B, H, -1),
+                                            flat(lo8)[:, :, N:].reshape(B, H, -1),
+                                            flat(hi8)[:, :, N:].reshape(B, H, -1)], axis=2)
         # then the power-of-two exponent E of each tile (int32 [B, H, n_pad/64])
-        out["k_exp"] = sec(L.k_expanded + BH * L.n_pad * 512, BH * (L.n_pad // 64), np.int32).reshape(
+        out["k_exp"] = sec(L.k_expanded + BH * tiles * 32768, BH * tiles, np.int32).reshape(
             B, H, L.n_pad // 64)
     return out
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 3
+    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 4
     for st in range(-6, 1):
         assert qs.status_string(st) not in ("", "unknown status")
     assert qs.status_string(-99) == "unknown status"

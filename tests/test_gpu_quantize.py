@@ -40,10 +40,10 @@ def check_quantize(qb, kb, vb, fmt, block_q, heads, label):
                 bad = np.argwhere(g.reshape(want.shape) != want)
                 pytest.fail(f"{label} {name} (b={b},h={h}): {len(bad)} mismatches, first at {bad[:3].tolist()}")
         if fmt == "fp4":
-            # the f16 pair the FP4 score MFMAs take: x = fp32 of the oracle's exact
+            # the operands the FP4 score MFMAs take: x = fp32 of the oracle's exact
             # code * scale, times 2^-E of its 64-key tile (E = biased exponent of the
             # tile's largest scale - 138, as documented in include/qsdpa.h), then
-            # hi = f16(x), lo = f16(x - hi) in fp32
+            # hi = f16(x), lo8 = E4M3(fp32(x - hi) * 2^5), hi8 = E4M3(hi * 2^-6)
             x = oracle.dequantize_qk(z.k_codes, z.k_scales, fmt, 16, 0, 0).astype(np.float32)
             sk = np.zeros((got["k_exp"].shape[2] * 64, 8), np.float32)
             sk[:N] = z.k_scales[0, 0]
@@ -53,11 +53,13 @@ def check_quantize(qb, kb, vb, fmt, block_q, heads, label):
                 pytest.fail(f"{label} k_exp (b={b},h={h}): {got['k_exp'][b, h][:8]} != {E[:8]}")
             x = np.ldexp(x, -np.repeat(E, 64)[:N, None]).astype(np.float32)
             hi = x.astype(np.float16)
-            lo = (x - hi.astype(np.float32)).astype(np.float16)
-            for name, want in (("k_hi", hi), ("k_lo", lo)):
+            lo = (x - hi.astype(np.float32)).astype(np.float32)
+            lo8 = oracle.encode(oracle.round_to(np.ldexp(lo.astype(np.float64), 5), oracle.E4M3), oracle.E4M3)
+            hi8 = oracle.encode(oracle.round_to(np.ldexp(hi.astype(np.float64), -6), oracle.E4M3), oracle.E4M3)
+            for name, want in (("k_hi", hi.view(np.uint16)), ("k_lo8", lo8), ("k_hi8", hi8)):
                 g = got[name][b, h]
-                if not np.array_equal(g, want.view(np.uint16)):
-                    bad = np.argwhere(g != want.view(np.uint16))
+                if not np.array_equal(g, want):
+                    bad = np.argwhere(g != want)
                     pytest.fail(f"{label} {name} (b={b},h={h}): {len(bad)} mismatches, first at {bad[:3].tolist()}")
     for name in ("q_codes_pad", "k_codes_pad", "v_codes_pad", "q_scales_pad", "k_scales_pad", "k_hilo_pad"):
         if name in got:
