@@ -3,7 +3,8 @@
 // quantizing Q itself from bf16), attn_mx_kernel (MXFP4 Q/K codes, scores on
 // the scaled MFMA in its FP4 format, same ring and schedule) and
 // attn_fp4_kernel (FP4 Q/K codes with fp32 scales per 16 channels, scores
-// from f16 hi/lo pairs).  What follows describes the structure all share.
+// from f16 hi parts plus FP8 hi/lo corrections).  What follows describes the
+// structure all share.
 //
 // Work split: one workgroup = 4 waves = 128 consecutive queries of one (b,h);
 // each wave owns 32 queries and walks all keys in steps of 64, in ascending

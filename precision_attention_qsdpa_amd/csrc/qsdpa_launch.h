@@ -29,7 +29,7 @@ struct LaunchArgs {
   uint8_t* v_codes;
   float* v_scales;
   float* v_amax;
-  uint8_t* k_expanded;   // FP4 mode: K as f16 hi/lo tiles
+  uint8_t* k_expanded;   // FP4 mode: K as f16 hi + E4M3 correction tiles
   void* stats_sum;
   void* stats_max;
 };

@@ -3,7 +3,7 @@
 // MXFP4 (E8M0 scale) codes of Q and K, per-channel FP8 codes of V written as
 // key-tiles in the order the attention kernel's value product consumes them,
 // and in FP4 mode K expanded once per head into the attention kernel's f16
-// hi/lo tiles.
+// hi and E4M3 correction tiles.
 //
 // All of these kernels are bound by HBM traffic; they read bf16 rows with
 // 16-byte loads, 16 threads per 256-byte token row.

@@ -81,9 +81,9 @@ def _round(x, a):
 def test_workspace_closed_form(B, H, N, fmt, bq):
     """One byte per Q/K code in FP8 mode (half a byte in the FP4 modes), one byte
     per V code, fp32 scales (one E8M0 byte per 32 channels in MXFP4 mode),
-    padded to 128 tokens, 256-byte aligned sections; in FP4 mode also the f16
-    hi/lo expansion of K (4 bytes per element) and an int32 exponent per 64-key
-    tile."""
+    padded to 128 tokens, 256-byte aligned sections; in FP4 mode also the
+    expansion of K (f16 hi plus the E4M3 lo8 and hi8: 4 bytes per element) and
+    an int32 exponent per 64-key tile."""
     p = qs.make_params(B, H, N, fmt=fmt, block_q=bq)
     L = qs.qsdpa_workspace_layout(p)
     BH, npad = B * H, _round(N, 128)
