@@ -35,19 +35,19 @@ def sample_rows(N, rng):
     return np.array(sorted(rows))
 
 
-def compare(out_bits, qb, kb, vb, fmt, block_q, heads, rows_of, label):
+def compare(out_bits, qb, kb, vb, fmt, block_q, heads, rows_of, label, tau=TAU):
     errs, raw_errs, exact_errs = [], [], []
     for b, h in heads:
         rows = rows_of(b, h)
         z = oracle.quantize(qb[b:b + 1, h:h + 1], kb[b:b + 1, h:h + 1], vb[b:b + 1, h:h + 1],
                             fmt=fmt, block_q=block_q, block_k=64)
-        want, bound = oracle.attend(z, TAU, 0, 0, rows, ambiguity=AMBIGUITY)
+        want, bound = oracle.attend(z, tau, 0, 0, rows, ambiguity=AMBIGUITY)
         got = oracle.bf16_bits_to_f64(out_bits[b, h, rows])
         raw = np.abs(got - want)
         raw_errs.append(raw)
         errs.append(np.maximum(raw - bound, 0.0))
         q, k, v = (oracle.bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb))
-        exact_errs.append(np.abs(got - oracle.exact_attention(q, k, v, TAU, rows)))
+        exact_errs.append(np.abs(got - oracle.exact_attention(q, k, v, tau, rows)))
     e = np.concatenate([x.ravel() for x in errs])
     x = np.concatenate([x.ravel() for x in exact_errs])
     rw = np.concatenate([x.ravel() for x in raw_errs])
@@ -269,6 +269,20 @@ def test_peaked_attention_large_logits(gpu_lib, fmt, shift):
     print(f"[forward] peaked {fmt} shift {shift}: max-abs {e.max():.3e} mean-abs {e.mean():.3e} "
           f"|O| max {np.abs(got).max():.2f}", flush=True)
     assert e.mean() <= MEAN_ABS
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+@pytest.mark.parametrize("tau", [0.02, 0.12])
+def test_softmax_scale_is_applied(gpu_lib, fmt, tau):
+    """A softmax scale other than 1/sqrt(128) = 0.088: flatter weights (0.02)
+    and sharper ones (0.12), against the oracle at the same scale."""
+    N = 777
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=N, seed=71)
+    params = qs.make_params(1, 2, N, fmt=fmt, block_q=128, softmax_scale=tau)
+    print(f"[forward] softmax scale {tau} fmt={fmt}", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    tau32 = float(np.float32(tau))   # the scale the library receives
+    compare(out, qb, kb, vb, fmt, 128, [(0, 0), (0, 1)], lambda b, h: np.arange(N), f"tau={tau}-{fmt}", tau=tau32)
 
 
 def test_forward_full_size_block_q_64(gpu_lib):
