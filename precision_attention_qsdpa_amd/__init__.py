@@ -128,12 +128,21 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _check_qkv(t, params: QsdpaParams, name: str):
+def _check_qkv(t, params: QsdpaParams, name: str, device):
     import torch
     shape = (params.batch, params.heads, params.seq_len, params.head_dim)
-    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
-        raise ValueError(f"{name} must be a contiguous CUDA bfloat16 tensor of shape {shape}, "
+    if (t.dtype != torch.bfloat16 or not t.is_cuda or t.device != device or not t.is_contiguous()
+            or tuple(t.shape) != shape):
+        raise ValueError(f"{name} must be a contiguous CUDA bfloat16 tensor of shape {shape} on {device}, "
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_workspace(ws, device):
+    """The workspace must be contiguous device memory on the tensors' GPU:
+    the library takes its address as a device pointer."""
+    if not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous CUDA tensor on {device}, got one on {ws.device}"
+                         f"{'' if ws.is_contiguous() else ' (not contiguous)'}")
 
 
 def empty_workspace(params: QsdpaParams, device=None):
@@ -147,18 +156,24 @@ def empty_workspace(params: QsdpaParams, device=None):
 
 def qsdpa_quantize(q, k, v, workspace, params: QsdpaParams, stream=None) -> None:
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_qkv(t, params, n)
-    st = load().qsdpa_quantize(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                               _stream(stream))
+        _check_qkv(t, params, n, q.device)
+    _check_workspace(workspace, q.device)
+    import torch
+    with torch.cuda.device(q.device):
+        st = load().qsdpa_quantize(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(stream))
     if st != QSDPA_OK:
         raise QsdpaError(st, "qsdpa_quantize")
 
 
 def qsdpa_attention(workspace, out, params: QsdpaParams, stream=None) -> None:
-    _check_qkv(out, params, "out")
-    st = load().qsdpa_attention(ctypes.byref(params), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), out.data_ptr(), _stream(stream))
+    _check_qkv(out, params, "out", out.device)
+    _check_workspace(workspace, out.device)
+    import torch
+    with torch.cuda.device(out.device):
+        st = load().qsdpa_attention(ctypes.byref(params), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), out.data_ptr(), _stream(stream))
     if st != QSDPA_OK:
         raise QsdpaError(st, "qsdpa_attention")
 
@@ -173,15 +188,17 @@ def qsdpa_forward(q, k, v, out=None, workspace=None, *, fmt: str = "fp8", block_
         params = make_params(B, H, N, fmt=fmt, block_q=block_q, block_k=block_k,
                              softmax_scale=softmax_scale, head_dim=Dh)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_qkv(t, params, n)
+        _check_qkv(t, params, n, q.device)
     if out is None:
         out = torch.empty_like(q)
-    _check_qkv(out, params, "out")
+    _check_qkv(out, params, "out", q.device)
     if workspace is None:
         workspace = empty_workspace(params, q.device)
-    st = load().qsdpa_forward(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                              _stream(stream))
+    _check_workspace(workspace, q.device)
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        st = load().qsdpa_forward(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
     if st != QSDPA_OK:
         raise QsdpaError(st, "qsdpa_forward")
     return out

@@ -135,3 +135,14 @@ def test_buffer_checks_before_any_launch():
     assert lib.qsdpa_quantize(ctypes.byref(p), 0x10000000, None, 0x30000000, 0x50000000, need, None) == \
         qs.QSDPA_ERR_INVALID_ARG
     assert lib.qsdpa_workspace_layout(ctypes.byref(p), None) == qs.QSDPA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors_before_the_library():
+    """q, k, v, out and the workspace must be CUDA tensors on one device: the
+    binding raises before any pointer reaches the library."""
+    import torch
+    q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="contiguous CUDA bfloat16"):
+        qs.qsdpa_forward(q, q, q)
+    with pytest.raises(ValueError, match="workspace must be a contiguous CUDA tensor"):
+        qs._check_workspace(torch.empty(64, dtype=torch.uint8), torch.device("cuda", 0))
