@@ -757,8 +757,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
     const int* __restrict__ kexp, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
     uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh, int prio_slots) {
   set_round_priority(prio_slots);
-  // ring: stages 0, 1 of expanded K tiles (hi then lo), then stages 0, 1 of V^T tiles: 80 KB,
-  // so that two workgroups share a CU's 160 KB
+  // ring: stages 0, 1 of expanded K tiles (f16 hi, then E4M3 corrections), then stages 0, 1
+  // of V^T tiles: 80 KB, so that two workgroups share a CU's 160 KB
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * (KXTILE + KTILE)];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KXTILE; };
   auto lds_v = [&](int S) -> uint8_t* { return ring + 2 * KXTILE + S * KTILE; };

@@ -82,10 +82,11 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 // whatever the input magnitude.
 __device__ __forceinline__ int fp4_norm_exp(float smax) { return (int)((__float_as_uint(smax) >> 23) & 0xffu) - 138; }
 
-// Bytes of one 64-key tile of FP4-mode K expanded to f16 hi + lo (2 x 16 KB),
-// and the byte offset of 8-channel chunk c of key row `row` inside the hi (or
-// lo) half: rows of 256 B, chunk c stored at position c ^ (row & 15), so the
-// 16 lanes that read one chunk column of 16 rows hit 16 different positions.
+// Bytes of one 64-key tile of FP4-mode K expanded to an f16 hi tile and an
+// E4M3 correction tile (2 x 16 KB), and the byte offset of 16-byte chunk c of
+// key row `row` inside either: rows of 256 B, chunk c stored at position
+// c ^ (row & 15), so the 16 lanes that read one chunk column of 16 rows hit
+// 16 different positions.
 constexpr int KXTILE = 2 * KSTEP * D * 2;
 __device__ __forceinline__ int kh_off(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
 
