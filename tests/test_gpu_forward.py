@@ -299,6 +299,37 @@ def test_forward_full_size_block_q_64(gpu_lib):
             "kontext1024-bq64")
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "fp4"])
+def test_offsets_beyond_4gib(gpu_lib, fmt):
+    """B*H = 8192 heads of 4608 tokens: each bf16 tensor is 9.7 GB, the FP8 code
+    sections 4.8 GB and the FP4 expansion of K 19 GB, so every byte offset past
+    2^32 must be formed in 64 bits.  Three heads spread over the batch are
+    checked against the oracle on sampled rows."""
+    B, H, N = 32, 256, 4608
+    free, _ = torch.cuda.mem_get_info()
+    if free < 100e9:
+        pytest.skip(f"needs about 80 GB of free device memory, {free / 1e9:.0f} GB free")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4608)
+    shape = (B, H, N, 128)
+    q = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    k += 3 * torch.randn((1, 1, 1, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    params = qs.make_params(B, H, N, fmt=fmt, block_q=128)
+    print(f"[forward] offsets beyond 4 GiB fmt={fmt} B={B} H={H} N={N}", flush=True)
+    out = qs.qsdpa_forward(q, k, v, params=params)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (B // 2, H // 3), (B - 1, H - 1)]
+    pick = lambda t: np.stack([from_dev(t[b, h]) for b, h in heads])[None]   # [1, 3, N, 128]
+    qb, kb, vb, ob = pick(q), pick(k), pick(v), pick(out)
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(3)
+    compare(ob, qb, kb, vb, fmt, 128, [(0, i) for i in range(3)], lambda b, h: sample_rows(N, rng),
+            f"4GiB-{fmt}")
+
+
 def test_concurrent_streams_match_serial(gpu_lib):
     """Two forwards on two streams at once (own inputs, outputs and
     workspaces) give the serial results bit for bit: the library keeps no
