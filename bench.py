@@ -24,6 +24,16 @@ sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0
+# The attention kernel's own MFMA roofline per mode: half of its flops are
+# Q.K^T, half P.V (FP8 in every mode), so its peak is the harmonic mean of the
+# two contractions' dense peaks.  Q.K^T runs on FP8 (5.0 PFLOP/s), on FP4 in
+# the MXFP4 mode (10.1) and, in the FP4 mode, on f16 MFMAs (2.5; the FP8
+# correction MFMAs come on top of that).
+_QK_PEAK = {"fp8": 5000.0, "mxfp4": 10100.0, "fp4": 2500.0}
+KERNEL_PEAK_TFLOPS = {m: 2.0 / (1.0 / p + 1.0 / FP8_PEAK_TFLOPS) for m, p in _QK_PEAK.items()}
+PEAK_BASIS = {"fp8": "dense FP8 MFMA (Q.K^T and P.V)",
+              "mxfp4": "Q.K^T at the dense FP4 peak, P.V at the dense FP8 peak (harmonic mean)",
+              "fp4": "Q.K^T at the dense f16 peak, P.V at the dense FP8 peak (harmonic mean)"}
 
 
 def parse():
@@ -225,7 +235,8 @@ def main():
                    "head_dim": 128, "qk_format": w.fmt, "block_q": w.block_q, "block_k": w.block_k,
                    "pct_fp8_peak": round(100.0 * tflops / FP8_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(attn_tflops, 2),
-                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+                     "peak": round(KERNEL_PEAK_TFLOPS[w.fmt], 1), "peak_basis": PEAK_BASIS[w.fmt],
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / KERNEL_PEAK_TFLOPS[w.fmt], 4),
                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
         "quantize": {"ms_per_launch": round(ms_quant, 4),
                      "algorithmic_GB_s": round(elem * quant_bpe / (ms_quant * 1e-3) / 1e9, 1),
