@@ -185,6 +185,23 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
 
+    # single steps, each between its own pair of events (after the timed region,
+    # so the clocks are already up): the median of 50, and the pages' protocol
+    # of 2 warm-up calls followed by the mean of 10
+    def single_steps(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        return [a.elapsed_time(b) for a, b in ev]
+    single = sorted(single_steps(50))
+    single_steps(2)
+    ten = single_steps(10)
+    per_step = {"median_of_50": round(single[25], 4), "min_of_50": round(single[0], 4),
+                "max_of_50": round(single[-1], 4), "mean_of_10_after_2_warmups": round(sum(ten) / 10, 4)}
+
     # the quantize pass and the dominant kernel (fused attention), timed alone;
     # the quantize pass runs first: it writes every workspace section the
     # attention reads (qsdpa_forward leaves the Q codes to the attention kernel)
@@ -242,6 +259,7 @@ def main():
                      "algorithmic_GB_s": round(elem * quant_bpe / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_peak_GB_s": HBM_PEAK_GBS},
         "wall_s_timed": round(wall, 3),
+        "per_step_ms": per_step,
     }
     if not args.no_shapes and w.name == "kontext1024":
         # the metric's other FLUX shapes (FP8): one line each, not the headline value
