@@ -128,6 +128,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _torch_stream(stream, device):
+    """The torch stream object the kernels will run on (the current stream of
+    ``device`` if None; a raw hipStream_t handle is wrapped)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 def _check_qkv(t, params: QsdpaParams, name: str, device):
     import torch
     shape = (params.batch, params.heads, params.seq_len, params.head_dim)
@@ -189,11 +200,16 @@ def qsdpa_forward(q, k, v, out=None, workspace=None, *, fmt: str = "fp8", block_
                              softmax_scale=softmax_scale, head_dim=Dh)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check_qkv(t, params, n, q.device)
-    if out is None:
-        out = torch.empty_like(q)
+    if out is None or workspace is None:
+        # allocated on the stream the kernels run on: the caching allocator
+        # then hands these blocks to no other stream's work while the kernels
+        # may still use them (the workspace is freed when this call returns)
+        with torch.cuda.stream(_torch_stream(stream, q.device)):
+            if out is None:
+                out = torch.empty_like(q)
+            if workspace is None:
+                workspace = empty_workspace(params, q.device)
     _check_qkv(out, params, "out", q.device)
-    if workspace is None:
-        workspace = empty_workspace(params, q.device)
     _check_workspace(workspace, q.device)
     with torch.cuda.device(q.device):   # the library launches on the current device
         st = load().qsdpa_forward(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -228,10 +228,10 @@ __device__ __forceinline__ void store_out(const v16f* o, float l, uint16_t* __re
 //   and issues the loads of K(t+4) and V(t+2).
 // Each wave issues 4 such loads per step, so at the end of step t a wave waits
 // until at most 8 of its loads are outstanding (those of steps t-1 and t),
-// which means K(t+2) and V(t) have landed, then joins the barrier.  The
-// barrier is a plain s_barrier: the only loads in flight across it are these
-// ring loads, which target stages no wave reads before the wait that covers
-// them.
+// which means K(t+2) and V(t) have landed (given the prologue's issue order,
+// ring_prologue), then joins the barrier.  The barrier is a plain s_barrier:
+// the only loads in flight across it are these ring loads, which target
+// stages no wave reads before the wait that covers them.
 // ---------------------------------------------------------------------------
 constexpr int NSTAGE = 4;
 
@@ -252,6 +252,27 @@ __device__ __forceinline__ void ring_copy16(const uint8_t* gbase, uint32_t voff,
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p);
 }
+
+// The ring's start: K(0), K(1), K(2), V(0), K(3), V(1), in that order, so
+// that from the first step on the copies go out as K(t+3), V(t) pairs: K(0)
+// K(1) K(2) V(0) | K(3) V(1) | K(4) V(2) | ...  (K(t+4) and V(t+2) issued
+// by step t).  A wave then has 2t + 8 copy groups (2 copies each) issued by
+// the end of step t, and a wait for at most 8 outstanding copies means the
+// first 2t + 4 groups landed, the last two of them K(t+2) and V(t): the
+// operands of step t+1.  Tiles past the last one repeat it.
+template <class RK, class RV>
+__device__ __forceinline__ void ring_prologue(RK ring_k, RV ring_v, int Tm1) {
+  ring_k(0, 0);
+  ring_k(min(1, Tm1), 1);
+  ring_k(min(2, Tm1), 2);
+  ring_v(0, 0);
+  ring_k(min(3, Tm1), 3);
+  ring_v(min(1, Tm1), 1);
+}
+
+// After the prologue's score reads of K(0): every wave's LDS reads have
+// returned before any wave passes, so step 0 may refill K stage 0.
+__device__ __forceinline__ void ring_release() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ void ring_barrier_wait8() {
   // s_waitcnt vmcnt(8) lgkmcnt(0): ring copies of the last two steps may stay
@@ -413,23 +434,20 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   // cover the copies.
   const int Tm1 = T - 1;
   if constexpr (!FUSE_Q) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
-  ring_k(0, 0);
-  ring_k(min(1, Tm1), 1);
-  ring_k(min(2, Tm1), 2);
-  ring_k(min(3, Tm1), 3);
-  ring_v(0, 0);
-  ring_v(min(1, Tm1), 1);
+  ring_prologue(ring_k, ring_v, Tm1);
   if constexpr (FUSE_Q) {
     load_q();
     cscale = tau_log2e * qscale;
   }
   *(u32x4*)(lds_v(3) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
   *(u32x4*)(lds_v(3) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
-  // K(0), K(1) landed (at most K(2), K(3), V(0), V(1) outstanding)
+  // K(0), K(1) landed (at most K(2), V(0), K(3), V(1) outstanding)
   __builtin_amdgcn_s_waitcnt(0x0070 | 8);
   asm volatile("s_barrier" ::: "memory");
   v16f sa[2], sb[2];
   scores(lds_k(0), sa, k_first(lds_k(0)));
+  // every wave has read K(0) before step 0 refills its stage
+  ring_release();
   v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;
 
@@ -649,12 +667,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
   // prologue as in the FP8 kernel (FUSE_Q: Q loaded after the ring copies)
   const int Tm1 = T - 1;
   if constexpr (!FUSE_Q) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
-  ring_k(0, 0);
-  ring_k(min(1, Tm1), 1);
-  ring_k(min(2, Tm1), 2);
-  ring_k(min(3, Tm1), 3);
-  ring_v(0, 0);
-  ring_v(min(1, Tm1), 1);
+  ring_prologue(ring_k, ring_v, Tm1);
   if constexpr (FUSE_Q) load_q();
   *(u32x4*)(lds_v(3) + tid * 16) = u32x4{0u, 0u, 0u, 0u};
   *(u32x4*)(lds_v(3) + tid * 16 + 4096) = u32x4{0u, 0u, 0u, 0u};
@@ -662,6 +675,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
   asm volatile("s_barrier" ::: "memory");
   v16f sa[2], sb[2];
   scores(lds_k(0), sa, k_first(lds_k(0)), k_scales(lds_k(0)));
+  ring_release();
   v8i pb_prev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;
 
