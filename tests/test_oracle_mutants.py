@@ -15,6 +15,7 @@ import oracle
 import oracle.formats
 import oracle.qsdpa
 import test_oracle_attention as A
+import test_oracle_fp4 as P4
 import test_oracle_formats as F
 import test_oracle_mx as M
 import test_oracle_quantize as Q
@@ -78,6 +79,16 @@ MUTANTS = [
     ("fp4_max_code_4", QS, "scales = np.where(_live(amax, 6.0), amax / np.float32(6.0), np.float32(0.0))",
      "scales = np.where(_live(amax, 6.0), amax / np.float32(4.0), np.float32(0.0))",
      [(Q.test_fp4_groups_and_nibble_order, {}), (Q.test_fp4_error_bound, {})]),
+    ("fp4_group_scales_reversed", QS,
+     "return (vals.reshape(N, D // FP4_GROUP, FP4_GROUP) * s[:, :, None]).reshape(N, D)",
+     "return (vals.reshape(N, D // FP4_GROUP, FP4_GROUP) * s[:, ::-1, None]).reshape(N, D)",
+     [(P4.test_fp4_dequantized_groups_by_loops, {}), (P4.test_fp4_dequantized_values_within_e2m1_bound_of_inputs, {}),
+      (P4.test_fp4_forward_close_to_exact_attention, {})]),
+    ("fp4_group_scales_dropped", QS,
+     "return (vals.reshape(N, D // FP4_GROUP, FP4_GROUP) * s[:, :, None]).reshape(N, D)",
+     "return vals",
+     [(P4.test_fp4_dequantized_groups_by_loops, {}), (P4.test_fp4_dequantized_values_within_e2m1_bound_of_inputs, {}),
+      (P4.test_fp4_forward_close_to_exact_attention, {})]),
     ("mx_exponent_minus_1", QS, "shared = (e - 1) - 2", "shared = (e - 1) - 1",
      [(M.test_shared_exponent_and_block_max_code, {"m": 1.5, "k": 0, "want": 6.0})]),
     ("mx_scale_bias_126", QS, "X = np.ldexp(1.0, byte.astype(np.int64) - E8M0_BIAS)",
@@ -102,7 +113,7 @@ MUTANTS = [
      [(F.test_e2m1_rounding_matches_bruteforce, {}), (F.test_e2m1_ties_and_saturation, {"x": 7.0, "want": 6.0})]),
 ]
 
-TARGETS = (oracle, QS, FM, A, F, M, Q)
+TARGETS = (oracle, QS, FM, A, F, M, P4, Q)
 
 
 def _load(mod, old, new):
