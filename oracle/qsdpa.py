@@ -254,24 +254,21 @@ def dequantize_qk(codes, scales, fmt: str, block: int, b: int, h: int) -> np.nda
 # 5-7: attention
 # --------------------------------------------------------------------------
 def online_softmax_av(S: np.ndarray, V: np.ndarray, *, step: int = SOFTMAX_STEP, quantize_p: bool = True,
-                      ambiguity: float = 0.0):
+                      trace: list | None = None):
     """Step 6 for fp64 scores S [R, N] and values V [N, D].
 
-    Returns (acc [R, D], l [R], amb [R, D]).  With ``quantize_p`` the weights
-    fed to the value product are E4M3(fp32(448 p)); without it they are
-    448 p exactly, so acc / (448 l) is then plain softmax(S) V.
+    Returns (acc [R, D], l [R]).  With ``quantize_p`` the weights fed to the
+    value product are E4M3(fp32(448 p)); without it they are 448 p exactly, so
+    acc / (448 l) is then plain softmax(S) V.
 
-    ``amb`` accumulates, like ``acc``, the weight gap |E4M3(v(1+e)) -
-    E4M3(v(1-e))| times |V| for every weight v = 448 p lying within a relative
-    distance e = ``ambiguity`` of an E4M3 rounding midpoint: an fp32 evaluation
-    of p may legitimately round such a weight either way, so amb bounds how far
-    a correct fp32 implementation can be from acc (zero when e = 0)."""
+    ``trace``, if a list, receives one record per step (for the tests that
+    bound how far a correct fp32 implementation may land from this result):
+    the first key j0, the running maxima before and after the step, alpha,
+    the unquantized p and the weights w."""
     R, N = S.shape
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     acc = np.zeros((R, V.shape[1]))
-    amb = np.zeros((R, V.shape[1]))
-    absV = np.abs(V)
     for j0 in range(0, N, step):
         Sb = S[:, j0:j0 + step]
         m_new = np.maximum(m, Sb.max(axis=1))
@@ -280,36 +277,37 @@ def online_softmax_av(S: np.ndarray, V: np.ndarray, *, step: int = SOFTMAX_STEP,
         if quantize_p:
             v = P_SCALE * p
             w = round_to(f32(v).astype(np.float64), E4M3)
-            if ambiguity > 0:
-                gap = (round_to(v * (1 + ambiguity), E4M3) - round_to(v * (1 - ambiguity), E4M3))
-                amb = alpha[:, None] * amb + gap @ absV[j0:j0 + step]
         else:
             w = P_SCALE * p
         l = alpha * l + p.sum(axis=1)
         acc = alpha[:, None] * acc + w @ V[j0:j0 + step]
+        if trace is not None:
+            trace.append({"j0": j0, "m_prev": m, "m": m_new, "alpha": alpha, "p": p, "w": w})
         m = m_new
-    return acc, l, amb
+    return acc, l
 
 
-def attend(qz: Quantized, tau: float, b: int, h: int, rows=None, *, ambiguity: float = 0.0):
+def attend(qz: Quantized, tau: float, b: int, h: int, rows=None, *, trace: dict | None = None):
     """Steps 5-7 for one (b, h).  Returns O as float64 bf16 values [R, D]
-    for the query rows ``rows`` (all rows if None).  With ``ambiguity`` > 0
-    returns (O, bound): bound [R, D] is how far O may move when the P codes
-    that lie within that relative distance of a rounding midpoint round the
-    other way (see ``online_softmax_av``)."""
+    for the query rows ``rows`` (all rows if None).
+
+    ``trace``, if a dict, receives the intermediates (for the tests): the
+    dequantized Q rows and K ("Qd", "Kd"), the scores "S", the V codes "Vc",
+    the V scales "sv", "acc", "l", the output before its bf16 rounding
+    "out", and the per-step records of ``online_softmax_av`` ("steps")."""
     Qd = dequantize_qk(qz.q_codes, qz.q_scales, qz.fmt, qz.block_q, b, h)
     Kd = dequantize_qk(qz.k_codes, qz.k_scales, qz.fmt, qz.block_k, b, h)
     if rows is not None:
         Qd = Qd[np.asarray(rows)]
     S = float(tau) * (Qd @ Kd.T)
     Vc = decode(qz.v_codes[b, h], E4M3)
-    acc, l, amb = online_softmax_av(S, Vc, ambiguity=ambiguity)
+    steps = [] if trace is not None else None
+    acc, l = online_softmax_av(S, Vc, trace=steps)
     sv = qz.v_scales[b, h].astype(np.float64)[None, :]
     out = acc * sv / (P_SCALE * l)[:, None]
-    o = bf16_bits_to_f64(f64_to_bf16_bits(out))
-    if ambiguity > 0:
-        return o, amb * sv / (P_SCALE * l)[:, None]
-    return o
+    if trace is not None:
+        trace.update(Qd=Qd, Kd=Kd, S=S, Vc=Vc, sv=sv[0], acc=acc, l=l, out=out, steps=steps)
+    return bf16_bits_to_f64(f64_to_bf16_bits(out))
 
 
 def forward(q_bits, k_bits, v_bits, *, fmt: str = FP8, block_q: int = 128, block_k: int = 64,

@@ -8,6 +8,7 @@ import torch
 
 import oracle
 import precision_attention_qsdpa_amd as qs
+import kernel_error
 from gpu_helpers import from_dev, run_forward, tiny_magnitude_inputs, to_dev
 from workloads import TAU, WORKLOADS, draw
 
@@ -15,14 +16,6 @@ pytestmark = pytest.mark.gpu
 
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
-# P codes whose fp64 weight lies within this relative distance of an E4M3
-# rounding midpoint may round either way in the kernel's fp32 softmax (logits
-# carry a few fp32 roundings of up to |s c| ~ 64, i.e. ~2e-5 relative in p):
-# either code is correct there, and the oracle bounds their effect on O.  The
-# FP8 MFMA also drops product bits below 2^-14 of the largest product of each
-# 64-term sum, which can flip a few codes farther out; on the workloads their
-# effect stays far inside the tolerance.
-AMBIGUITY = 2.0 ** -13
 
 
 def sample_rows(N, rng):
@@ -35,27 +28,48 @@ def sample_rows(N, rng):
     return np.array(sorted(rows))
 
 
-def compare(out_bits, qb, kb, vb, fmt, block_q, heads, rows_of, label, tau=TAU):
-    errs, raw_errs, exact_errs = [], [], []
+def compare(out_bits, qb, kb, vb, fmt, block_q, heads, rows_of, label, tau=TAU, edge=None):
+    """The GPU output against the oracle on the given heads and rows: raw
+    max-abs <= 1e-2 and mean-abs <= 1e-3 on the bf16 O (asserted), and the
+    error against exact fp64 attention (printed).
+
+    ``edge`` names an edge case whose raw max-abs may exceed 1e-2 for a
+    recorded cause (a P code within the kernel's rounding of an E4M3 midpoint,
+    or a bf16 step larger than 1e-2).  Then the raw mean-abs is still
+    asserted, and so is the midpoint-adjusted check: max(|got - want| -
+    allowed, 0) <= 1e-2, with ``allowed`` the bound of kernel_error (derived
+    from the matrix cores' measured truncation and the fp32 roundings)."""
+    raw_errs, exact_errs, adj_errs = [], [], []
     for b, h in heads:
         rows = rows_of(b, h)
         z = oracle.quantize(qb[b:b + 1, h:h + 1], kb[b:b + 1, h:h + 1], vb[b:b + 1, h:h + 1],
                             fmt=fmt, block_q=block_q, block_k=64)
-        want, bound = oracle.attend(z, tau, 0, 0, rows, ambiguity=AMBIGUITY)
+        want = oracle.attend(z, tau, 0, 0, rows)
         got = oracle.bf16_bits_to_f64(out_bits[b, h, rows])
         raw = np.abs(got - want)
         raw_errs.append(raw)
-        errs.append(np.maximum(raw - bound, 0.0))
+        if edge is not None or raw.max() > MAX_ABS:
+            _, allowed, diag = kernel_error.output_allowance(z, tau, 0, 0, rows)
+            adj_errs.append(np.maximum(raw - allowed, 0.0))
+            if raw.max() > MAX_ABS:
+                i, d = np.unravel_index(raw.argmax(), raw.shape)
+                print(f"[forward] {label} (b={b}, h={h}): raw max-abs {raw.max():.3e} at row {rows[i]} channel {d} "
+                      f"(got {got[i, d]}, oracle {want[i, d]}, allowed {allowed[i, d]:.3e}); "
+                      f"{diag['ambiguous_codes']} P codes within the kernel's rounding of a midpoint", flush=True)
         q, k, v = (oracle.bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb))
         exact_errs.append(np.abs(got - oracle.exact_attention(q, k, v, tau, rows)))
-    e = np.concatenate([x.ravel() for x in errs])
-    x = np.concatenate([x.ravel() for x in exact_errs])
     rw = np.concatenate([x.ravel() for x in raw_errs])
-    print(f"[forward] {label}: vs oracle max {e.max():.3e} mean {e.mean():.3e} (raw max {rw.max():.3e} "
-          f"mean {rw.mean():.3e}) | vs exact fp64 max {x.max():.3e} mean {x.mean():.3e}", flush=True)
-    assert np.all(np.isfinite(e))
-    assert e.max() <= MAX_ABS, f"{label}: max-abs {e.max()}"
-    assert e.mean() <= MEAN_ABS, f"{label}: mean-abs {e.mean()}"
+    x = np.concatenate([x.ravel() for x in exact_errs])
+    adj = np.concatenate([x.ravel() for x in adj_errs]) if adj_errs else None
+    print(f"[forward] {label}: vs oracle max {rw.max():.3e} mean {rw.mean():.3e}"
+          + (f" (midpoint-adjusted max {adj.max():.3e})" if adj is not None else "")
+          + f" | vs exact fp64 max {x.max():.3e} mean {x.mean():.3e}", flush=True)
+    assert np.all(np.isfinite(rw))
+    assert rw.mean() <= MEAN_ABS, f"{label}: mean-abs {rw.mean()}"
+    if edge is None:
+        assert rw.max() <= MAX_ABS, f"{label}: max-abs {rw.max()}"
+    else:
+        assert adj.max() <= MAX_ABS, f"{label} ({edge}): midpoint-adjusted max-abs {adj.max()}"
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -91,6 +105,17 @@ def test_forward_long_sequence(gpu_lib, fmt):
     compare(out, qb, kb, vb, fmt, 128, [(0, 0)], lambda b, h: rows, f"long-{fmt}")
 
 
+# Ragged cases whose raw max-abs exceeds 1e-2, and why.  N = 129, FP8,
+# block_q = 64, batch 1, query 65, channel 96: the weight of key 3 in the first
+# step is 448 p = 304.000731, 2.4e-6 above the E4M3 midpoint 304 between codes
+# 288 and 320.  The oracle codes it 320; the kernel's score, whose MFMA drops
+# product bits below 2^-14 of the largest product, puts it just below (288).
+# One code step of 32 times |V| = 3.14 over 448 l (l = 10.6), scaled down by
+# the later steps, moves O by 0.0122 (kernel_error's CPU emulation of the
+# kernel arithmetic gives the same 1.221e-2 at the same element).
+RAGGED_EDGE = {(129, "fp8", 64): "P code at an E4M3 midpoint"}
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 100, 127, 129, 1000])
 @pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp8", 128), ("fp4", 128), ("mxfp4", 128)])
 def test_forward_ragged_lengths(gpu_lib, N, fmt, bq):
@@ -98,7 +123,8 @@ def test_forward_ragged_lengths(gpu_lib, N, fmt, bq):
     params = qs.make_params(2, 1, N, fmt=fmt, block_q=bq)
     print(f"[forward] ragged N={N} fmt={fmt} bq={bq}", flush=True)
     out = run_forward(qb, kb, vb, params)
-    compare(out, qb, kb, vb, fmt, bq, [(0, 0), (1, 0)], lambda b, h: np.arange(N), f"N={N} {fmt} bq={bq}")
+    compare(out, qb, kb, vb, fmt, bq, [(0, 0), (1, 0)], lambda b, h: np.arange(N), f"N={N} {fmt} bq={bq}",
+            edge=RAGGED_EDGE.get((N, fmt, bq)))
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
@@ -176,7 +202,7 @@ def test_deterministic_and_in_bounds(gpu_lib):
     o = obig[guard:guard + numel].view(torch.bfloat16).view(1, 3, N, 128)
     ws = wbig[4096:4096 + need]
     outs = []
-    for _ in range(5):
+    for _ in range(20):
         qs.qsdpa_forward(q, k, v, out=o, workspace=ws, params=params)
         torch.cuda.synchronize()
         outs.append(from_dev(o).copy())
@@ -247,11 +273,15 @@ def test_power_of_two_input_scaling(gpu_lib, fmt, shift):
 def test_peaked_attention_large_logits(gpu_lib, fmt, shift):
     """Q times 2^shift: logits up to about 110 (shift 4) and 1750 (shift 8)
     in log2 units, so most rows put nearly all weight on one key and |O|
-    reaches 4.  The output stays finite and within the mean-abs 1e-3 of the
-    oracle.  Max-abs is printed, not asserted: at |O| >= 2 one bf16 step is
-    already 2^-6 > 1e-2, and the FP8 MFMA drops product bits below 2^-14 of
-    the largest product of each 64-term sum, which moves large logits enough
-    to flip a few P codes the other way."""
+    reaches 4.  An edge case for the raw max-abs, for two recorded causes:
+    where |O| >= 2 one bf16 step is 2^-6 > 1e-2, and the one-hot rows of
+    shift 8 land exactly on bf16 ties (l = 1, O = a V value times sV), which a
+    last-bit difference of the fp32 epilogue rounds the other way; and in the
+    rows of shift 4 with l near 1.3, one P code step at an E4M3 midpoint moves
+    O by up to 2 % of |V| (the FP8 MFMA drops product bits below 2^-14 of the
+    largest product, which at these logits moves them by up to ~0.2 in log2
+    units).  Asserted: finite, raw mean-abs <= 1e-3, the midpoint-adjusted
+    max-abs, and that at most 0.5 % of the elements are more than 1e-2 off."""
     N = 300
     qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=N, seed=45)
     q2 = scale_bits(qb, shift)
@@ -260,15 +290,14 @@ def test_peaked_attention_large_logits(gpu_lib, fmt, shift):
     out = run_forward(q2, kb, vb, params)
     got = oracle.bf16_bits_to_f64(out)
     assert np.all(np.isfinite(got))
-    errs = []
-    for h in range(2):
-        z = oracle.quantize(q2[:, h:h + 1], kb[:, h:h + 1], vb[:, h:h + 1], fmt=fmt, block_q=128, block_k=64)
-        want, bound = oracle.attend(z, TAU, 0, 0, ambiguity=AMBIGUITY)
-        errs.append(np.maximum(np.abs(got[0, h] - want) - bound, 0.0))
-    e = np.concatenate([x.ravel() for x in errs])
-    print(f"[forward] peaked {fmt} shift {shift}: max-abs {e.max():.3e} mean-abs {e.mean():.3e} "
-          f"|O| max {np.abs(got).max():.2f}", flush=True)
-    assert e.mean() <= MEAN_ABS
+    compare(out, q2, kb, vb, fmt, 128, [(0, 0), (0, 1)], lambda b, h: np.arange(N), f"peaked-{fmt}-{shift}",
+            edge="bf16 steps above 1e-2 and P codes at E4M3 midpoints")
+    want = np.stack([oracle.attend(oracle.quantize(q2[:, h:h + 1], kb[:, h:h + 1], vb[:, h:h + 1], fmt=fmt,
+                                                   block_q=128, block_k=64), TAU, 0, 0) for h in range(2)])
+    frac = np.mean(np.abs(got[0] - want) > MAX_ABS)
+    print(f"[forward] peaked {fmt} shift {shift}: {frac:.4%} of elements above 1e-2, |O| max {np.abs(got).max():.2f}",
+          flush=True)
+    assert frac <= 0.005
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
@@ -355,3 +384,26 @@ def test_concurrent_streams_match_serial(gpu_lib):
     torch.cuda.synchronize()
     for i, (o, _) in enumerate(outs):
         assert np.array_equal(from_dev(o), serial[i % 2]), f"stream result {i} differs"
+
+
+def test_forward_on_another_stream_without_workspace(gpu_lib):
+    """qsdpa_forward on a stream other than the current one, with out and
+    workspace left to the binding: they are allocated on that stream, so the
+    memory the caller allocates on the current stream right after the call
+    (while the kernels may still be running) never overlaps the workspace."""
+    N, H = 6000, 6
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=H, seq_len=N, seed=77)
+    params = qs.make_params(1, H, N, fmt="fp8", block_q=128)
+    ref = run_forward(qb, kb, vb, params)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    need = qs.qsdpa_workspace_bytes(params)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("[forward] other stream, binding-allocated workspace", flush=True)
+    for _ in range(3):
+        out = qs.qsdpa_forward(q, k, v, params=params, stream=s)   # the current stream is not s
+        junk = [torch.full((need,), 0x77, dtype=torch.uint8, device="cuda") for _ in range(3)]
+        s.synchronize()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(out), ref)
+        del junk
