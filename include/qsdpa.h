@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSDPA_ABI_VERSION 4
+#define QSDPA_ABI_VERSION 5
 #define QSDPA_HEAD_DIM 128
 
 /* Status codes (return values). */
@@ -64,6 +64,11 @@ extern "C" {
 #define QSDPA_ERR_WORKSPACE_TOO_SMALL (-4) /* ws_bytes < qsdpa_workspace_bytes() */
 #define QSDPA_ERR_ALIAS (-5)               /* O overlaps an input or the workspace */
 #define QSDPA_ERR_HIP (-6)                 /* a kernel launch failed */
+#define QSDPA_ERR_SCRATCH_TOO_SMALL (-7)   /* qsdpa_forward_noalloc: workspace > QSDPA_SCRATCH_BYTES */
+
+/* Size of the static scratch array of qsdpa_forward_noalloc (96 MiB per GPU):
+ * enough for the Kontext workload [1, 24, 8704, 128] in FP8 and MXFP4 mode. */
+#define QSDPA_SCRATCH_BYTES (96u << 20)
 
 /* Q/K precision.  P and V are FP8 E4M3 in every mode.
  * MXFP4 (beyond the pages' FP4): E2M1 codes with one shared E8M0 (power of
@@ -179,6 +184,25 @@ int qsdpa_attention(const qsdpa_params* p, const void* workspace, size_t ws_byte
  */
 int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o,
                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * qsdpa_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and result, bit for bit, with the workspace taken
+ * from a static device array of QSDPA_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends.  No allocation of any kind.
+ * q, k, v, o as for qsdpa_forward, on the current device.
+ *   - Returns QSDPA_ERR_SCRATCH_TOO_SMALL (nothing enqueued) when
+ *     qsdpa_workspace_bytes(p) exceeds QSDPA_SCRATCH_BYTES.
+ *   - Every call on one GPU shares that GPU's array: calls whose work may
+ *     overlap on one GPU (two streams, or two threads) race on it and must be
+ *     serialized by the caller.  The array keeps the last call's contents;
+ *     no call depends on them.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress); QSDPA_ERR_HIP if that fails.
+ */
+int qsdpa_forward_noalloc(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,8 @@ QSDPA_ERR_ALIGNMENT = -3
 QSDPA_ERR_WORKSPACE_TOO_SMALL = -4
 QSDPA_ERR_ALIAS = -5
 QSDPA_ERR_HIP = -6
+QSDPA_ERR_SCRATCH_TOO_SMALL = -7
+QSDPA_SCRATCH_BYTES = 96 << 20   # the static scratch array of qsdpa_forward_noalloc, per GPU
 QSDPA_QK_FP8_E4M3 = 0
 QSDPA_QK_FP4_E2M1 = 1
 QSDPA_QK_MXFP4_E2M1 = 2
@@ -29,7 +31,8 @@ QK_FORMATS = {"fp8": QSDPA_QK_FP8_E4M3, "fp4": QSDPA_QK_FP4_E2M1, "mxfp4": QSDPA
 HEAD_DIM = 128
 
 EXPORTS = ("qsdpa_abi_version", "qsdpa_status_string", "qsdpa_validate_params", "qsdpa_workspace_bytes",
-           "qsdpa_workspace_layout", "qsdpa_quantize", "qsdpa_attention", "qsdpa_forward")
+           "qsdpa_workspace_layout", "qsdpa_quantize", "qsdpa_attention", "qsdpa_forward",
+           "qsdpa_forward_noalloc")
 
 
 class QsdpaParams(ctypes.Structure):
@@ -39,7 +42,7 @@ class QsdpaParams(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
-ABI_VERSION = 4   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
+ABI_VERSION = 5   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
 
 
 class QsdpaLayout(ctypes.Structure):
@@ -85,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.qsdpa_attention.argtypes = [P, vp, sz, vp, vp]
     lib.qsdpa_forward.restype = ctypes.c_int
     lib.qsdpa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsdpa_forward_noalloc.restype = ctypes.c_int
+    lib.qsdpa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp]
     if lib.qsdpa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {lib.qsdpa_abi_version()}, this binding expects "
                            f"{ABI_VERSION}: rebuild it with `python -m precision_attention_qsdpa_amd.build`")
@@ -217,4 +222,19 @@ def qsdpa_forward(q, k, v, out=None, workspace=None, *, fmt: str = "fp8", block_
                                   _stream(stream))
     if st != QSDPA_OK:
         raise QsdpaError(st, "qsdpa_forward")
+    return out
+
+
+def qsdpa_forward_noalloc(q, k, v, out, params: QsdpaParams, stream=None):
+    """qsdpa_forward with the workspace in the library's static scratch array
+    (no allocation by the library or here; ``out`` is the caller's).  Calls
+    whose work may overlap on one GPU share that array and must not overlap."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _check_qkv(t, params, n, q.device)
+    import torch
+    with torch.cuda.device(q.device):
+        st = load().qsdpa_forward_noalloc(ctypes.byref(params), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), _stream(stream))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_forward_noalloc")
     return out

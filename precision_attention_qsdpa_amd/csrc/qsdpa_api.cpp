@@ -147,6 +147,7 @@ const char* qsdpa_status_string(int status) {
     case QSDPA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case QSDPA_ERR_ALIAS: return "output overlaps an input or the workspace";
     case QSDPA_ERR_HIP: return "HIP launch failure";
+    case QSDPA_ERR_SCRATCH_TOO_SMALL: return "the problem needs more workspace than the static scratch buffer holds";
     default: return "unknown status";
   }
 }
@@ -195,6 +196,15 @@ int qsdpa_attention(const qsdpa_params* p, const void* workspace, size_t ws_byte
 
 int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o, void* workspace,
                   size_t ws_bytes, void* stream) {
+  return qsdpa::forward_impl(p, q, k, v, o, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace qsdpa {
+
+int forward_impl(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o, void* workspace,
+                 size_t ws_bytes, void* stream) {
   int st = check_params(p);
   if (st != QSDPA_OK) return st;
   qsdpa_layout L;
@@ -211,4 +221,4 @@ int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const voi
   return launch_status();
 }
 
-}  // extern "C"
+}  // namespace qsdpa

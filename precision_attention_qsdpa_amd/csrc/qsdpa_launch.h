@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/qsdpa.h"
+
 namespace qsdpa {
 
 constexpr int STATS_ROWS = 256;  // tokens per range of the statistics pass
@@ -36,5 +38,10 @@ struct LaunchArgs {
 
 void launch_quantize(const LaunchArgs& a, hipStream_t s);
 void launch_attention(const LaunchArgs& a, hipStream_t s);
+
+// qsdpa_forward on a caller-chosen workspace (argument checks, launches,
+// status); shared by qsdpa_forward and the entry point on the static scratch.
+int forward_impl(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o, void* workspace,
+                 size_t ws_bytes, void* stream);
 
 }  // namespace qsdpa

@@ -28,8 +28,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 4
-    for st in range(-6, 1):
+    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 5
+    for st in range(-7, 1):
         assert qs.status_string(st) not in ("", "unknown status")
     assert qs.status_string(-99) == "unknown status"
 
@@ -146,3 +146,18 @@ def test_binding_rejects_host_tensors_before_the_library():
         qs.qsdpa_forward(q, q, q)
     with pytest.raises(ValueError, match="workspace must be a contiguous CUDA tensor"):
         qs._check_workspace(torch.empty(64, dtype=torch.uint8), torch.device("cuda", 0))
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch_array():
+    """qsdpa_forward_noalloc returns before any GPU call when the workspace
+    would exceed the static scratch array (or the parameters are invalid)."""
+    lib = qs.load()
+    fits = qs.make_params(1, 24, 8704, fmt="fp8")
+    assert qs.qsdpa_workspace_bytes(fits) <= qs.QSDPA_SCRATCH_BYTES
+    big = qs.make_params(2, 24, 16896, fmt="fp8")
+    assert qs.qsdpa_workspace_bytes(big) > qs.QSDPA_SCRATCH_BYTES
+    assert lib.qsdpa_forward_noalloc(ctypes.byref(big), 256, 512, 768, 1 << 40, None) == \
+        qs.QSDPA_ERR_SCRATCH_TOO_SMALL
+    bad = qs.make_params(1, 2, 320, block_q=96)
+    assert lib.qsdpa_forward_noalloc(ctypes.byref(bad), 256, 512, 768, 1 << 40, None) == qs.QSDPA_ERR_UNSUPPORTED
+    assert "static scratch" in qs.status_string(qs.QSDPA_ERR_SCRATCH_TOO_SMALL)
