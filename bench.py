@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the other FLUX shapes of the metric (N = 4608 and 16896, FP8)")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="(b,h) pairs of the CPU oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="(b,h) pairs of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_attn_fp8_kontext1024.json"),
@@ -53,32 +53,65 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, heads: int, got_bits):
-    """The oracle, single process with single-threaded BLAS, on the first
-    ``heads`` (b, h) pairs of batch 0 of the workload: quantize of each head
-    and every query row against every key, timed.  Then, untimed, the error of
-    the GPU output on those heads (``got_bits``, bf16 bits [heads, N, 128])
-    against the oracle's output and against exact attention.  Returns the
-    baseline record and the accuracy record."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+# At most this many oracle workers: the host share of one GPU on the machines
+# this runs on.
+MAX_CPU_WORKERS = 16
 
+
+def _worker_init():
+    """Oracle worker: single-threaded BLAS, so that the workers are the
+    parallelism."""
+    global _LIMITS
+    from threadpoolctl import threadpool_limits
+    _LIMITS = threadpool_limits(limits=1)
+
+
+def _oracle_head(task):
+    """Quantize + attention of one (b, h) pair through the oracle (runs in a
+    worker process).  Returns the output [N, 128] and the seconds it took."""
+    qh, kh, vh, fmt, block_q, block_k = task
     import oracle
-    from workloads import TAU, draw
+    from workloads import TAU
+    t0 = time.perf_counter()
+    z = oracle.quantize(qh, kh, vh, fmt=fmt, block_q=block_q, block_k=block_k)
+    out = oracle.attend(z, TAU, 0, 0)
+    return out, time.perf_counter() - t0
+
+
+def start_cpu_pool(heads: int):
+    """Worker processes for the oracle, forked now: before this process makes
+    any GPU call, so the workers never touch the GPU.  One per host core this
+    process may run on (os.sched_getaffinity), at most MAX_CPU_WORKERS and at
+    most one per head of the sample."""
+    import multiprocessing as mp
+    n = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS, heads))
+    return mp.get_context("fork").Pool(n, initializer=_worker_init), n
+
+
+def cpu_baseline(w, heads: int, got_bits, pool, workers: int):
+    """The oracle on the first ``heads`` (b, h) pairs of batch 0 of the
+    workload, one pair per task over ``workers`` worker processes (each with
+    single-threaded BLAS): quantize of each head and every query row against
+    every key, timed from the first task out to the last result back.  Then,
+    untimed, the error of the GPU output on those heads (``got_bits``, bf16
+    bits [heads, N, 128]) against the oracle's output and against exact
+    attention.  Returns the baseline record and the accuracy record."""
+    import numpy as np
+
+    from workloads import draw
 
     qb, kb, vb = draw(w, batch=1, heads=heads)   # the same tensors as heads 0.. of batch 0
-    outs = np.empty((heads, w.seq_len, 128))
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for h in range(heads):
-            z = oracle.quantize(qb[:, h:h + 1], kb[:, h:h + 1], vb[:, h:h + 1], fmt=w.fmt,
-                                block_q=w.block_q, block_k=w.block_k)
-            outs[h] = oracle.attend(z, TAU, 0, 0)
-        dt = time.perf_counter() - t0
+    tasks = [(qb[:, h:h + 1], kb[:, h:h + 1], vb[:, h:h + 1], w.fmt, w.block_q, w.block_k) for h in range(heads)]
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_head, tasks, chunksize=1)
+    dt = time.perf_counter() - t0
+    outs = np.stack([r[0] for r in res])
+    cpu_s = sum(r[1] for r in res)
     flops = 4.0 * heads * w.seq_len ** 2 * 128
-    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
            "sample": f"{heads} of the {w.batch * w.heads} (b,h) pairs of {w.name}, all {w.seq_len} query rows "
-                     f"(quantize + attention), {dt:.1f} s wall, single-threaded NumPy"}
+                     f"(quantize + attention), one pair per task on {workers} worker processes with "
+                     f"single-threaded NumPy: {dt:.1f} s wall, {cpu_s:.1f} s of CPU work"}
     return rec, accuracy(w, got_bits, outs, (qb, kb, vb))
 
 
@@ -143,6 +176,9 @@ def main():
               "the path shards by (batch, head) with no exchange: each GPU would run this same "
               "kernel on its share of the heads", file=sys.stderr)
         sys.exit(2)
+    pool = workers = None
+    if not args.no_cpu_baseline and not args.copy_calibration:
+        pool, workers = start_cpu_pool(args.cpu_heads)   # before the first GPU call
     import torch
 
     if args.copy_calibration:
@@ -275,7 +311,9 @@ def main():
     if not args.no_cpu_baseline:
         heads = min(args.cpu_heads, w.heads)
         got_bits = out[0, :heads].contiguous().view(torch.int16).cpu().numpy().view("uint16")
-        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline(w, heads, got_bits)
+        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline(w, heads, got_bits, pool, workers)
+        pool.close()
+        pool.join()
     print(json.dumps(rec), flush=True)
 
 
