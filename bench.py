@@ -24,16 +24,19 @@ sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0
-# The attention kernel's own MFMA roofline per mode: half of its flops are
-# Q.K^T, half P.V (FP8 in every mode), so its peak is the harmonic mean of the
-# two contractions' dense peaks.  Q.K^T runs on FP8 (5.0 PFLOP/s), on FP4 in
-# the MXFP4 mode (10.1) and, in the FP4 mode, on f16 MFMAs (2.5; the FP8
-# correction MFMAs come on top of that).
-_QK_PEAK = {"fp8": 5000.0, "mxfp4": 10100.0, "fp4": 2500.0}
-KERNEL_PEAK_TFLOPS = {m: 2.0 / (1.0 / p + 1.0 / FP8_PEAK_TFLOPS) for m, p in _QK_PEAK.items()}
+# The attention kernel's roofline per mode.  FP8: dense FP8 MFMA.  MXFP4: half
+# of the flops are Q.K^T on the FP4 MFMA (10.1 PFLOP/s dense) and half P.V on
+# FP8 (5.0), so its peak is the harmonic mean of the two.  FP4 (fp32 scales per
+# 16 channels): the dense FP8 peak, since its P.V is FP8 and its exact Q.K^T
+# runs on f16 MFMAs plus FP8 correction MFMAs (the FP4 peak, 10.1, is noted in
+# the record; the hardware's scaled FP4 MFMA cannot apply fp32 scales).
+FP4_PEAK_TFLOPS = 10100.0
+KERNEL_PEAK_TFLOPS = {"fp8": FP8_PEAK_TFLOPS, "fp4": FP8_PEAK_TFLOPS,
+                      "mxfp4": 2.0 / (1.0 / FP4_PEAK_TFLOPS + 1.0 / FP8_PEAK_TFLOPS)}
 PEAK_BASIS = {"fp8": "dense FP8 MFMA (Q.K^T and P.V)",
               "mxfp4": "Q.K^T at the dense FP4 peak, P.V at the dense FP8 peak (harmonic mean)",
-              "fp4": "Q.K^T at the dense f16 peak, P.V at the dense FP8 peak (harmonic mean)"}
+              "fp4": "dense FP8 MFMA (P.V is FP8; the exact per-16-channel Q.K^T runs on f16 + FP8 "
+                     "MFMAs); dense FP4 peak 10100 TFLOP/s"}
 
 
 def parse():
@@ -238,23 +241,30 @@ def main():
     per_step = {"median_of_50": round(single[25], 4), "min_of_50": round(single[0], 4),
                 "max_of_50": round(single[-1], 4), "mean_of_10_after_2_warmups": round(sum(ten) / 10, 4)}
 
-    # the quantize pass and the dominant kernel (fused attention), timed alone;
-    # the quantize pass runs first: it writes every workspace section the
-    # attention reads (qsdpa_forward leaves the Q codes to the attention kernel)
+    # the quantize pass and the dominant kernel, timed alone on the same
+    # stream.  The dominant kernel is the attention kernel of the timed step
+    # (qsdpa_forward's, which quantizes Q in its prologue): it runs alone as
+    # qsdpa_attention_bf16q on the K/V codes the timed steps left in the
+    # workspace.  qsdpa_attention (on Q codes from qsdpa_quantize) is timed too.
     n_attn = max(args.steps, 20)
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    (a0, a1), (b0, b1), (c0, c1) = ev(), ev(), ev()
+    a0.record(stream)
+    for _ in range(n_attn):
+        qs.qsdpa_attention_bf16q(q, ws, out, params, stream=stream)
+    a1.record(stream)
     b0.record(stream)
     for _ in range(n_attn):
         qs.qsdpa_quantize(q, k, v, ws, params, stream=stream)
     b1.record(stream)
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
+    c0.record(stream)
     for _ in range(n_attn):
         qs.qsdpa_attention(ws, out, params, stream=stream)
-    a1.record(stream)
+    c1.record(stream)
     torch.cuda.synchronize(dev)
     ms_attn = a0.elapsed_time(a1) / n_attn
     ms_quant = b0.elapsed_time(b1) / n_attn
+    ms_attn_codes = c0.elapsed_time(c1) / n_attn
 
     flops = w.flops
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -266,7 +276,7 @@ def main():
         if tj.get("workload") == w.name and tj.get("kernel_source_sha") == kernel_sha():
             traffic = tj.get("hbm_bytes_per_launch")
     elem = w.batch * w.heads * w.seq_len * 128
-    kernel = {"fp8": "attn_fp8_kernel", "fp4": "attn_fp4_kernel", "mxfp4": "attn_mx_kernel"}[w.fmt]
+    kernel = {"fp8": "attn_fp8_kernel<true>", "fp4": "attn_fp4_kernel<true>", "mxfp4": "attn_mx_kernel<true>"}[w.fmt]
     # quantize pass bytes per element: Q, K, V bf16 read (6) + K, V re-read by the
     # statistics pass (4) + codes and scales written; FP4 mode also reads the K
     # codes and scales again (0.75) and writes their f16 hi/lo expansion (4)
@@ -290,7 +300,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(attn_tflops, 2),
                      "peak": round(KERNEL_PEAK_TFLOPS[w.fmt], 1), "peak_basis": PEAK_BASIS[w.fmt],
                      "unit": "TFLOP/s", "frac": round(attn_tflops / KERNEL_PEAK_TFLOPS[w.fmt], 4),
-                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
+                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4),
+                     "ms_per_launch_on_q_codes": round(ms_attn_codes, 4)},
         "quantize": {"ms_per_launch": round(ms_quant, 4),
                      "algorithmic_GB_s": round(elem * quant_bpe / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_peak_GB_s": HBM_PEAK_GBS},

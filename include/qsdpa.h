@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSDPA_ABI_VERSION 5
+#define QSDPA_ABI_VERSION 6
 #define QSDPA_HEAD_DIM 128
 
 /* Status codes (return values). */
@@ -177,10 +177,23 @@ int qsdpa_attention(const qsdpa_params* p, const void* workspace, size_t ws_byte
                     void* stream);
 
 /*
+ * Steps 5-7 with Q given as bf16 [B,H,N,128]: the attention kernel quantizes
+ * Q itself (step 3 for Q, with the quantize pass's blocks and operations, so
+ * O is bit-identical to qsdpa_attention after qsdpa_quantize), on the K and V
+ * codes, scales and statistics of a workspace that qsdpa_quantize or
+ * qsdpa_forward filled with the same params and the same K and V.  The
+ * workspace's q_codes and q_scales sections are neither read nor written.
+ * This is the attention kernel of qsdpa_forward on its own (for example to
+ * attend several query sets to keys and values quantized once).
+ */
+int qsdpa_attention_bf16q(const qsdpa_params* p, const void* q, const void* workspace, size_t ws_bytes,
+                          void* o, void* stream);
+
+/*
  * qsdpa_quantize followed by qsdpa_attention on the same stream: O is
- * bit-identical to the two calls.  In FP8 and MXFP4 modes the attention
- * kernel quantizes Q itself (the same blocks and operations), so the q_codes
- * and q_scales sections of the workspace are not written by this call.
+ * bit-identical to the two calls.  The attention kernel quantizes Q itself
+ * (as qsdpa_attention_bf16q), so the q_codes and q_scales sections of the
+ * workspace are not written by this call.
  */
 int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o,
                   void* workspace, size_t ws_bytes, void* stream);

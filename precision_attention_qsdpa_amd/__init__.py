@@ -32,7 +32,7 @@ HEAD_DIM = 128
 
 EXPORTS = ("qsdpa_abi_version", "qsdpa_status_string", "qsdpa_validate_params", "qsdpa_workspace_bytes",
            "qsdpa_workspace_layout", "qsdpa_quantize", "qsdpa_attention", "qsdpa_forward",
-           "qsdpa_forward_noalloc")
+           "qsdpa_forward_noalloc", "qsdpa_attention_bf16q")
 
 
 class QsdpaParams(ctypes.Structure):
@@ -42,7 +42,7 @@ class QsdpaParams(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
-ABI_VERSION = 5   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
+ABI_VERSION = 6   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
 
 
 class QsdpaLayout(ctypes.Structure):
@@ -88,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.qsdpa_attention.argtypes = [P, vp, sz, vp, vp]
     lib.qsdpa_forward.restype = ctypes.c_int
     lib.qsdpa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsdpa_attention_bf16q.restype = ctypes.c_int
+    lib.qsdpa_attention_bf16q.argtypes = [P, vp, vp, sz, vp, vp]
     lib.qsdpa_forward_noalloc.restype = ctypes.c_int
     lib.qsdpa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp]
     if lib.qsdpa_abi_version() != ABI_VERSION:
@@ -192,6 +194,22 @@ def qsdpa_attention(workspace, out, params: QsdpaParams, stream=None) -> None:
                                     workspace.numel() * workspace.element_size(), out.data_ptr(), _stream(stream))
     if st != QSDPA_OK:
         raise QsdpaError(st, "qsdpa_attention")
+
+
+def qsdpa_attention_bf16q(q, workspace, out, params: QsdpaParams, stream=None) -> None:
+    """Attention of bf16 ``q`` on the K/V codes in ``workspace`` (filled by
+    qsdpa_quantize or qsdpa_forward with the same params); the kernel
+    quantizes Q itself."""
+    _check_qkv(q, params, "q", q.device)
+    _check_qkv(out, params, "out", q.device)
+    _check_workspace(workspace, q.device)
+    import torch
+    with torch.cuda.device(q.device):
+        st = load().qsdpa_attention_bf16q(ctypes.byref(params), q.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), out.data_ptr(),
+                                          _stream(stream))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_attention_bf16q")
 
 
 def qsdpa_forward(q, k, v, out=None, workspace=None, *, fmt: str = "fp8", block_q: int = 128,

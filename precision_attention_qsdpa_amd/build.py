@@ -38,18 +38,34 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libqsdpa.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# The race-detection build: the same sources with QSDPA_RING_STRESS, which
+# makes every wave sleep pseudo-random times where the attention kernels'
+# tile ring hands stages between waves (its output must be bit-identical).
+STRESS_LIB = os.path.join(PKG, "libqsdpa_stress.so")
+
+
+def _compile(out: str, extra: list, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + FLAGS + extra + ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libqsdpa.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libqsdpa.so, and the race-detection build
+    libqsdpa_stress.so (always recompiles both)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as ex:
+        jobs = [ex.submit(_compile, LIB, [], verbose),
+                ex.submit(_compile, STRESS_LIB, ["-DQSDPA_RING_STRESS=1"], verbose)]
+        for j in jobs:
+            j.result()
     return LIB
 
 

@@ -199,6 +199,25 @@ int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const voi
   return qsdpa::forward_impl(p, q, k, v, o, workspace, ws_bytes, stream);
 }
 
+int qsdpa_attention_bf16q(const qsdpa_params* p, const void* q, const void* workspace, size_t ws_bytes, void* o,
+                          void* stream) {
+  int st = check_params(p);
+  if (st != QSDPA_OK) return st;
+  qsdpa_layout L;
+  make_layout(p, &L);
+  st = check_buffers(p, L, nullptr, nullptr, nullptr, o, workspace, ws_bytes, false, true);
+  if (st != QSDPA_OK) return st;
+  if (!q) return QSDPA_ERR_INVALID_ARG;
+  if (!aligned(q, 16)) return QSDPA_ERR_ALIGNMENT;
+  const uint64_t tbytes = (uint64_t)p->batch * p->heads * p->seq_len * QSDPA_HEAD_DIM * 2;
+  if (overlaps(o, tbytes, q, tbytes) || overlaps(q, tbytes, workspace, L.total)) return QSDPA_ERR_ALIAS;
+  (void)hipGetLastError();
+  qsdpa::LaunchArgs a = make_args(p, L, q, nullptr, nullptr, o, workspace);
+  a.fuse_q = true;
+  qsdpa::launch_attention(a, (hipStream_t)stream);
+  return launch_status();
+}
+
 }  // extern "C"
 
 namespace qsdpa {
@@ -213,8 +232,8 @@ int forward_impl(const qsdpa_params* p, const void* q, const void* k, const void
   if (st != QSDPA_OK) return st;
   (void)hipGetLastError();
   qsdpa::LaunchArgs a = make_args(p, L, q, k, v, o, workspace);
-  // FP8 and MXFP4: Q is quantized inside the attention kernel, bit-identically
-  a.fuse_q = !a.fp4;
+  // Q is quantized inside the attention kernel, bit-identically
+  a.fuse_q = true;
   qsdpa::launch_quantize(a, (hipStream_t)stream);
   if (launch_status() != QSDPA_OK) return QSDPA_ERR_HIP;
   qsdpa::launch_attention(a, (hipStream_t)stream);

@@ -253,6 +253,32 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p);
 }
 
+#ifdef QSDPA_RING_STRESS
+// Race-detection build of the library (libqsdpa_stress.so): at each point
+// where the tile ring hands stages between waves, every wave sleeps for a
+// pseudo-random 0, 64, 128, 256 or 448 cycles, drawn per (workgroup, wave,
+// step, site).  Waves then reach the ring's waits and barriers in orders the
+// normal build rarely produces; with every wait in place the output stays
+// bit-identical to the normal build's, which a GPU test checks.
+__device__ __forceinline__ void ring_stress(int t, int site) {
+  uint32_t h = (uint32_t)blockIdx.x * 0x9E3779B1u +
+               (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 0x85EBCA77u +
+               (uint32_t)t * 0xC2B2AE3Du + (uint32_t)site * 0x27D4EB2Fu;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  switch (h & 7u) {
+    case 1: __builtin_amdgcn_s_sleep(1); break;
+    case 2: __builtin_amdgcn_s_sleep(2); break;
+    case 3: __builtin_amdgcn_s_sleep(4); break;
+    case 4: __builtin_amdgcn_s_sleep(7); break;
+    default: break;
+  }
+}
+#else
+__device__ __forceinline__ void ring_stress(int, int) {}
+#endif
+
 // The ring's start: K(0), K(1), K(2), V(0), K(3), V(1), in that order, so
 // that from the first step on the copies go out as K(t+3), V(t) pairs: K(0)
 // K(1) K(2) V(0) | K(3) V(1) | K(4) V(2) | ...  (K(t+4) and V(t+2) issued
@@ -262,6 +288,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // operands of step t+1.  Tiles past the last one repeat it.
 template <class RK, class RV>
 __device__ __forceinline__ void ring_prologue(RK ring_k, RV ring_v, int Tm1) {
+  ring_stress(-1, 0);
   ring_k(0, 0);
   ring_k(min(1, Tm1), 1);
   ring_k(min(2, Tm1), 2);
@@ -272,9 +299,13 @@ __device__ __forceinline__ void ring_prologue(RK ring_k, RV ring_v, int Tm1) {
 
 // After the prologue's score reads of K(0): every wave's LDS reads have
 // returned before any wave passes, so step 0 may refill K stage 0.
-__device__ __forceinline__ void ring_release() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void ring_release() {
+  ring_stress(-1, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-__device__ __forceinline__ void ring_barrier_wait8() {
+__device__ __forceinline__ void ring_barrier_wait8(int t) {
+  ring_stress(t, 3);
   // s_waitcnt vmcnt(8) lgkmcnt(0): ring copies of the last two steps may stay
   // in flight; every LDS read of this wave has returned before the barrier,
   // so a stage can be refilled right after it
@@ -459,6 +490,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     constexpr int S = decltype(st)::value;   // t % 4
     const v8i a00 = k_first(lds_k((S + 1) & 3));
     rescale(alpha_prev);
+    ring_stress(t, 2);
     ring_k(min(t + 4, Tm1), S);
     ring_v(min(t + 2, Tm1), (S + 2) & 3);
     scores(lds_k((S + 1) & 3), s_next, a00);
@@ -471,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
       __builtin_amdgcn_sched_group_barrier(0x402, 19, 0);         // VALU
     }
     kscn = ksc[t + 1];
-    ring_barrier_wait8();
+    ring_barrier_wait8(t);
   };
   int t = 0;
   for (; t + 4 < T; t += 4) {
@@ -486,13 +518,14 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     const int S = tt & 3;
     const v8i a00 = k_first(lds_k((S + 1) & 3));
     rescale(alpha_prev);
+    ring_stress(tt, 2);
     ring_k(min(tt + 4, Tm1), S);
     ring_v(min(tt + 2, Tm1), (S + 2) & 3);
     scores(lds_k((S + 1) & 3), s_next, a00);
     pv(pb_prev, lds_v((S + 3) & 3));
     pb_prev = softmax(tt, s_cur, std::true_type{}, alpha_prev);
     kscn = ksc[tt + 1];
-    ring_barrier_wait8();
+    ring_barrier_wait8(tt);
   };
   auto last = [&](int tl, v16f* s_cur) {
     const int S = tl & 3;
@@ -502,6 +535,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     const v8i pb = (tl + 1) * KSTEP <= N ? softmax(tl, s_cur, std::true_type{}, alpha)
                                          : softmax(tl, s_cur, std::false_type{}, alpha);
     // V(tl) is in stage S (issued at step tl-2 or in the prologue): wait for every ring copy
+    ring_stress(tl, 4);
     __builtin_amdgcn_s_waitcnt(0x0070);
     asm volatile("s_barrier" ::: "memory");
     rescale(alpha);
@@ -684,6 +718,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
     const v8i a00 = k_first(lds_k((S + 1) & 3));
     const uint32_t ksw = k_scales(lds_k((S + 1) & 3));
     rescale(alpha_prev);
+    ring_stress(t, 2);
     ring_k(min(t + 4, Tm1), S);
     ring_v(min(t + 2, Tm1), (S + 2) & 3);
     scores(lds_k((S + 1) & 3), s_next, a00, ksw);
@@ -694,7 +729,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 22, 0);   // VALU
     }
-    ring_barrier_wait8();
+    ring_barrier_wait8(t);
   };
   int t = 0;
   for (; t + 4 < T; t += 4) {
@@ -708,12 +743,13 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
     const v8i a00 = k_first(lds_k((S + 1) & 3));
     const uint32_t ksw = k_scales(lds_k((S + 1) & 3));
     rescale(alpha_prev);
+    ring_stress(tt, 2);
     ring_k(min(tt + 4, Tm1), S);
     ring_v(min(tt + 2, Tm1), (S + 2) & 3);
     scores(lds_k((S + 1) & 3), s_next, a00, ksw);
     pv(pb_prev, lds_v((S + 3) & 3));
     pb_prev = softmax(tt, s_cur, std::true_type{}, alpha_prev);
-    ring_barrier_wait8();
+    ring_barrier_wait8(tt);
   };
   auto last = [&](int tl, v16f* s_cur) {
     const int S = tl & 3;
@@ -722,6 +758,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
     float alpha;
     const v8i pb = (tl + 1) * KSTEP <= N ? softmax(tl, s_cur, std::true_type{}, alpha)
                                          : softmax(tl, s_cur, std::false_type{}, alpha);
+    ring_stress(tl, 4);
     __builtin_amdgcn_s_waitcnt(0x0070);
     asm volatile("s_barrier" ::: "memory");
     rescale(alpha);
@@ -766,10 +803,17 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
 // softmax and its MFMAs alternate, and the other wave of the SIMD fills the
 // gaps.
 // ---------------------------------------------------------------------------
+// FUSE_Q: Q arrives as bf16 (qx), and each lane makes the codes and fp32
+// scales of the 8 sixteen-channel groups of its query with the quantize
+// pass's operations (block maximum, IEEE divisions 6/amax and amax/6, fp32
+// product, clamp, E2M1 conversion), so the result is bit-identical to reading
+// the pass's codes (qc, qs).  Both lanes of a query make all 8 groups.
+template <bool FUSE_Q>
 __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
-    const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint8_t* __restrict__ kx,
-    const int* __restrict__ kexp, const uint8_t* __restrict__ vc, const float* __restrict__ vs,
-    uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e, int tiles_per_bh, int prio_slots) {
+    const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint16_t* __restrict__ qx,
+    const uint8_t* __restrict__ kx, const int* __restrict__ kexp, const uint8_t* __restrict__ vc,
+    const float* __restrict__ vs, uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e,
+    int tiles_per_bh, int prio_slots) {
   set_round_priority(prio_slots);
   // ring: stages 0, 1 of expanded K tiles (f16 hi, then E4M3 corrections), then stages 0, 1
   // of V^T tiles: 80 KB, so that two workgroups share a CU's 160 KB
@@ -797,10 +841,41 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
   float cq;
   {
     const size_t qrow = (size_t)bh * n_pad + q0 + r;
+    // scale and the two code words (channels 16c .. 16c + 7, then + 8 .. + 15) of each group
     float sc[8], smax = 0.f;
+    uint32_t cw[8][2];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      sc[c] = qs[qrow * 8 + c];
+      if constexpr (FUSE_Q) {
+        const int q = q0 + r;
+        u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+        if (q < N) {
+          const u32x4* src = (const u32x4*)(qx + ((size_t)bh * N + q) * D + 16 * c);
+          w0 = src[0];
+          w1 = src[1];
+        }
+        float val[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          val[2 * j] = bf16_lo(w0[j]);
+          val[2 * j + 1] = bf16_hi(w0[j]);
+          val[8 + 2 * j] = bf16_lo(w1[j]);
+          val[8 + 2 * j + 1] = bf16_hi(w1[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(val[j]));
+        const float inv = FP4_MAX / amax;   // +inf for amax = 0 or below FP4_MAX / FLT_MAX: zero codes
+        const bool live = inv < INFINITY;
+        sc[c] = live ? amax / FP4_MAX : 0.f;
+        cw[c][0] = live ? e2m1_word8(val, inv) : 0u;
+        cw[c][1] = live ? e2m1_word8(val + 8, inv) : 0u;
+      } else {
+        sc[c] = qs[qrow * 8 + c];
+        const u32x2 w = *(const u32x2*)(qc + qrow * 64 + 8 * c);
+        cw[c][0] = w[0];
+        cw[c][1] = w[1];
+      }
       smax = fmaxf(smax, sc[c]);
     }
     const int EQ = fp4_norm_exp(smax);
@@ -810,17 +885,21 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
       asm volatile("" : "+v"(x));
       return ldexpf(x, -EQ);
     };
+    // lane-dependent choices as bit selects (an indexed pick would put the
+    // arrays in scratch memory)
+    const uint32_t gm = 0u - (uint32_t)g;
+    auto pick = [&](uint32_t a, uint32_t b) { return a ^ ((a ^ b) & gm); };   // g ? b : a
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint32_t w = *(const uint32_t*)(qc + qrow * 64 + 8 * c + 4 * g);
+      const uint32_t w = pick(cw[c][0], cw[c][1]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qhi[c][e] = (_Float16)scaled((w >> (4 * e)) & 15u, sc[c]);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int c = 2 * p + g;
-      const u32x2 w = *(const u32x2*)(qc + qrow * 64 + 8 * c);
-      const float scale = qs[qrow * 8 + c];
+      // chunk c = 2p + g
+      const u32x2 w = {pick(cw[2 * p][0], cw[2 * p + 1][0]), pick(cw[2 * p][1], cw[2 * p + 1][1])};
+      const float scale = __uint_as_float(pick(__float_as_uint(sc[2 * p]), __float_as_uint(sc[2 * p + 1])));
       float h8[16], l8[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -914,6 +993,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
   v16f s[2];
   scores(lds_k(0), s);
   int ken = kebase[0];
+  ring_stress(-1, 1);
   __builtin_amdgcn_s_waitcnt(0x0070);
   asm volatile("s_barrier" ::: "memory");
 
@@ -926,6 +1006,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
   // MFMAs.
   for (int t = 0; t < T; ++t) {
     const int S = t & 1;
+    ring_stress(t, 2);
     if (t + 1 < T) {
       ring_k(min(t + 2, Tm1), S);
       ring_v(t + 1, S ^ 1);
@@ -940,6 +1021,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
       scores(lds_k(S ^ 1), s);
       ken = kebase[t + 1];
     }
+    ring_stress(t, 3);
     __builtin_amdgcn_s_waitcnt(0x0070);   // this step's copies landed, LDS reads done
     asm volatile("s_barrier" ::: "memory");
   }
@@ -974,10 +1056,10 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
                                     a.n_pad, tl, tiles, slots);
   } else if (a.fp4) {
     const int ktiles = a.n_pad / KSTEP;
-    attn_fp4_kernel<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, a.k_expanded,
-                                                (const int*)(a.k_expanded + (size_t)BH * ktiles * KXTILE),
-                                                a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl,
-                                                tiles, slots);
+    auto kern = a.fuse_q ? attn_fp4_kernel<true> : attn_fp4_kernel<false>;
+    kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_expanded,
+                                    (const int*)(a.k_expanded + (size_t)BH * ktiles * KXTILE), a.v_codes,
+                                    a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles, slots);
   } else {
     auto kern = a.fuse_q ? attn_fp8_kernel<true> : attn_fp8_kernel<false>;
     kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_codes, a.k_scales,

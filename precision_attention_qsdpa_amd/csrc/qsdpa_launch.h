@@ -15,7 +15,7 @@ struct LaunchArgs {
   int block_q;
   bool fp4;   // 16-channel FP4 with fp32 scales
   bool mx;    // MXFP4: 32-channel blocks with E8M0 scales
-  bool fuse_q;   // FP8, MXFP4: the attention kernel quantizes Q (the quantize pass skips it)
+  bool fuse_q;   // the attention kernel quantizes Q from bf16 (the quantize pass skips it)
   float softmax_scale;
   int stats_splits;
   int q_scale_count, k_scale_count;

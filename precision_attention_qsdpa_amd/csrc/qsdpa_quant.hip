@@ -159,15 +159,16 @@ __device__ __forceinline__ void fp8_block(const uint16_t* __restrict__ x, const 
 
 // ---------------------------------------------------------------------------
 // FP4 codes: one thread per (token, 16-channel group).  grid = (n_pad/32, BH, 2)
-// (z = 0: Q, z = 1: smoothed K), block = 256 = 32 tokens x 8 groups.
+// (z = 0: Q, z = 1: smoothed K; first_z = 1 and grid z = 1 when the attention
+// kernel quantizes Q itself), block = 256 = 32 tokens x 8 groups.
 // Codes [BH][n_pad][64] (even channel in the low nibble), scales [BH][n_pad][8].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_qk_fp4_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
     uint8_t* __restrict__ qc, float* __restrict__ qs, uint8_t* __restrict__ kc,
-    float* __restrict__ ks, int N, int n_pad) {
+    float* __restrict__ ks, int N, int n_pad, int first_z) {
   const int bh = last_first(blockIdx.y);
-  const bool is_k = blockIdx.z == 1;
+  const bool is_k = blockIdx.z + first_z == 1;
   const uint16_t* x = is_k ? k : q;
   uint8_t* codes = is_k ? kc : qc;
   float* scales = is_k ? ks : qs;
@@ -474,9 +475,11 @@ void launch_quantize(const LaunchArgs& a, hipStream_t s) {
         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_mean, a.v_amax, a.q_codes,
         (uint8_t*)a.q_scales, a.k_codes, (uint8_t*)a.k_scales, a.v_codes, a.seq_len, a.n_pad, first);
   } else if (a.fp4) {
-    quant_qk_fp4_kernel<<<dim3(a.n_pad / 32, BH, 2), 256, 0, s>>>(
+    // the Q groups are skipped when the attention kernel quantizes Q
+    const int first_z = a.fuse_q ? 1 : 0;
+    quant_qk_fp4_kernel<<<dim3(a.n_pad / 32, BH, 2 - first_z), 256, 0, s>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.k, a.k_mean, a.q_codes, a.q_scales, a.k_codes,
-        a.k_scales, a.seq_len, a.n_pad);
+        a.k_scales, a.seq_len, a.n_pad, first_z);
     expand_k_fp4_kernel<<<dim3(vtiles, BH), 256, 0, s>>>(a.k_codes, a.k_scales, a.k_expanded,
                                                         (int*)(a.k_expanded + (size_t)BH * vtiles * KXTILE), a.n_pad);
     quant_v_kernel<<<dim3(vtiles, BH), 256, 0, s>>>((const uint16_t*)a.v, a.v_amax, a.v_codes, a.seq_len,

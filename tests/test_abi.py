@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "qsdpa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qsdpa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qsdpa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 5
+    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 6
     for st in range(-7, 1):
         assert qs.status_string(st) not in ("", "unknown status")
     assert qs.status_string(-99) == "unknown status"

@@ -238,6 +238,30 @@ def test_split_calls_equal_forward(gpu_lib, fmt, bq, N):
     assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("fmt,bq,N", [("fp8", 128, 777), ("fp8", 64, 300), ("fp4", 128, 300), ("fp4", 128, 1),
+                                       ("mxfp4", 128, 300), ("mxfp4", 128, 129)])
+def test_attention_bf16q_equals_attention_on_codes(gpu_lib, fmt, bq, N):
+    """qsdpa_attention_bf16q (the attention kernel quantizing bf16 Q in its
+    prologue) on the K/V codes of a qsdpa_quantize workspace equals
+    qsdpa_attention on that workspace's Q codes, bit for bit (one Q block of
+    the N = 300 cases is all zeros, and in FP4 mode one token of a group)."""
+    qb, kb, vb = draw(WORKLOADS["tiny"], heads=2, seq_len=N, seed=91 + N)
+    if N == 300:
+        qb = qb.copy()
+        qb[:, :, 128:256] = 0
+        qb[:, 1, 17, 32:48] = 0
+    params = qs.make_params(1, 2, N, fmt=fmt, block_q=bq)
+    print(f"[forward] attention with bf16 Q fmt={fmt} bq={bq} N={N}", flush=True)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    ws = qs.empty_workspace(params)
+    qs.qsdpa_quantize(q, k, v, ws, params)
+    ref, got = torch.empty_like(q), torch.empty_like(q)
+    qs.qsdpa_attention(ws, ref, params)
+    qs.qsdpa_attention_bf16q(q, ws, got, params)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 def scale_bits(bits, e):
     """bf16 bit patterns times 2^e (exact for the normal values used here)."""
     x = np.ldexp((bits.astype(np.uint32) << 16).view(np.float32), e).astype(np.float32)
