@@ -13,7 +13,7 @@ from .formats import BF16, E2M1, E4M3, bf16_bits_to_f64, decode, encode, f64_to_
 from .qsdpa import (E8M0_BIAS, FP4, FP4_GROUP, FP8, MX_BLOCK, MXFP4, P_SCALE, SOFTMAX_STEP, Quantized, attend,
                     channel_stats, dequantize_qk, exact_attention, forward, online_softmax_av, quantize,
                     quantize_fp4_groups, quantize_fp8_blocks, quantize_mxfp4_blocks, quantize_v, smooth_k,
-                    unpack_fp4)
+                    unpack_fp4, VC_RHO, vc_count, vc_forward, vc_select, vc_token_error)
 
 __all__ = [
     "BF16", "E2M1", "E4M3", "E8M0_BIAS", "FP4", "FP4_GROUP", "FP8", "MXFP4", "MX_BLOCK", "P_SCALE",
@@ -21,4 +21,5 @@ __all__ = [
     "attend", "bf16_bits_to_f64", "channel_stats", "decode", "dequantize_qk", "encode",
     "exact_attention", "f64_to_bf16_bits", "forward", "online_softmax_av", "quantize",
     "quantize_fp4_groups", "quantize_fp8_blocks", "quantize_v", "round_to", "smooth_k", "unpack_fp4",
+    "VC_RHO", "vc_count", "vc_forward", "vc_select", "vc_token_error",
 ]

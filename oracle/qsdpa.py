@@ -52,6 +52,17 @@ head dimension D = 128, queries i and keys j:
 The step of 64 keys matters: P's codes are taken relative to the running
 maximum, so a different step gives different codes.
 
+Selective correction (VC-Attention-style)
+-----------------------------------------
+The VisualGen article (FLUX 3 Image Klein Base, devotd.net, "왜 이런 차이가
+나나") names VC-Attention FP8 with rho = 0.005 as FP8 attention that corrects
+only the tokens with a large error, and says no more.  The reading taken
+here: the tokens are the query tokens (rows of O); a token's error is its own
+FP8 quantization error, e_i = sum_d (q_id - code_id s_i)^2; per (b, h) the
+k = ceil(rho N) tokens with the largest e_i (ties to the lower index) get the
+unquantized softmax attention of the bf16 inputs in place of their quantized
+row.
+
 MXFP4 mode (beyond the pages)
 -----------------------------
 The pages' FP4 scheme has an fp32 scale per 16 channels.  The MXFP4 mode
@@ -320,6 +331,57 @@ def forward(q_bits, k_bits, v_bits, *, fmt: str = FP8, block_q: int = 128, block
         for h in range(H):
             out[b, h] = f64_to_bf16_bits(attend(qz, tau, b, h))
     return out
+
+
+# --------------------------------------------------------------------------
+# Selective correction of the high-error tokens (VC-Attention-style)
+# --------------------------------------------------------------------------
+VC_RHO = 0.005   # fraction of tokens corrected
+
+
+def vc_count(n_tokens: int, rho: float) -> int:
+    """Tokens corrected per (b, h): k = ceil(rho N), at least 1 and at most N."""
+    return min(n_tokens, max(1, math.ceil(rho * n_tokens - 1e-9)))
+
+
+def vc_token_error(qz: Quantized, q_bits, b: int, h: int) -> np.ndarray:
+    """Per query token i of (b, h): e_i = sum_d (q_id - code_id * s_i)^2, the
+    squared L2 norm of the token's own FP8 quantization error (q the bf16
+    input, code * s its dequantized value), summed exactly (math.fsum)."""
+    if qz.fmt != FP8:
+        raise ValueError("the selective correction is defined for the FP8 mode")
+    q = bf16_bits_to_f64(q_bits[b, h])
+    dq = q - dequantize_qk(qz.q_codes, qz.q_scales, FP8, qz.block_q, b, h)   # exact in fp64
+    return np.array([math.fsum((row * row).tolist()) for row in dq])
+
+
+def vc_select(err: np.ndarray, k: int) -> np.ndarray:
+    """The k tokens with the largest error, ties to the lower index; returned
+    in ascending index order."""
+    order = sorted(range(len(err)), key=lambda i: (-err[i], i))
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
+def vc_forward(q_bits, k_bits, v_bits, *, rho: float = VC_RHO, block_q: int = 128, block_k: int = 64,
+               tau: float = float(np.float32(1.0 / math.sqrt(128.0)))):
+    """FP8 quantized attention with the high-error tokens corrected: per
+    (b, h), the k = ceil(rho N) query tokens whose own quantization error
+    (vc_token_error) is largest get the unquantized softmax attention of the
+    bf16 inputs (fp64, rounded to bf16) in place of their quantized row.
+    Returns (O bf16 bits [B,H,N,D], selected rows [B,H,k])."""
+    qz = quantize(q_bits, k_bits, v_bits, fmt=FP8, block_q=block_q, block_k=block_k)
+    B, H, N, D = q_bits.shape
+    kk = vc_count(N, rho)
+    out = np.empty((B, H, N, D), dtype=np.uint16)
+    sel = np.empty((B, H, kk), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            o = attend(qz, tau, b, h)
+            sel[b, h] = vc_select(vc_token_error(qz, q_bits, b, h), kk)
+            q, k, v = (bf16_bits_to_f64(x[b, h]) for x in (q_bits, k_bits, v_bits))
+            o[sel[b, h]] = bf16_bits_to_f64(f64_to_bf16_bits(exact_attention(q, k, v, tau, sel[b, h])))
+            out[b, h] = f64_to_bf16_bits(o)
+    return out, sel
 
 
 def exact_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float, rows=None) -> np.ndarray:

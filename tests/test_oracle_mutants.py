@@ -19,6 +19,7 @@ import test_oracle_fp4 as P4
 import test_oracle_formats as F
 import test_oracle_mx as M
 import test_oracle_quantize as Q
+import test_oracle_vc as VC
 
 QS, FM = oracle.qsdpa, oracle.formats
 
@@ -94,6 +95,19 @@ MUTANTS = [
     ("mx_scale_bias_126", QS, "X = np.ldexp(1.0, byte.astype(np.int64) - E8M0_BIAS)",
      "X = np.ldexp(1.0, byte.astype(np.int64) - 126)",
      [(M.test_shared_exponent_and_block_max_code, {"m": 1.5, "k": 0, "want": 6.0})]),
+    # selective correction
+    ("vc_selects_smallest", QS, "key=lambda i: (-err[i], i))", "key=lambda i: (err[i], i))",
+     [(VC.test_selection_matches_brute_force_with_ties, {})]),
+    ("vc_ties_to_higher_index", QS, "key=lambda i: (-err[i], i))", "key=lambda i: (-err[i], -i))",
+     [(VC.test_selection_matches_brute_force_with_ties, {})]),
+    ("vc_error_not_squared", QS, "math.fsum((row * row).tolist())", "math.fsum(np.abs(row).tolist())",
+     [(VC.test_token_error_on_known_codes, {})]),
+    ("vc_count_floor", QS, "max(1, math.ceil(rho * n_tokens - 1e-9))", "max(1, math.floor(rho * n_tokens))",
+     [(VC.test_count_is_ceil_rho_n, {"n": 8704, "rho": 0.005, "want": 44})]),
+    ("vc_rows_not_corrected", QS,
+     "o[sel[b, h]] = bf16_bits_to_f64(f64_to_bf16_bits(exact_attention(q, k, v, tau, sel[b, h])))",
+     "o[sel[b, h]] = o[sel[b, h]]",
+     [(VC.test_all_tokens_corrected_is_exact_attention, {}), (VC.test_correction_lowers_the_error_of_its_rows, {})]),
     # format codecs
     ("round_half_away", FM, "r = np.rint(a / step) * step", "r = np.floor(a / step + 0.5) * step",
      [(F.test_e4m3_rounding_matches_torch_and_bruteforce, {}),
@@ -113,7 +127,7 @@ MUTANTS = [
      [(F.test_e2m1_rounding_matches_bruteforce, {}), (F.test_e2m1_ties_and_saturation, {"x": 7.0, "want": 6.0})]),
 ]
 
-TARGETS = (oracle, QS, FM, A, F, M, P4, Q)
+TARGETS = (oracle, QS, FM, A, F, M, P4, Q, VC)
 
 
 def _load(mod, old, new):
