@@ -308,6 +308,25 @@ def main():
         "wall_s_timed": round(wall, 3),
         "per_step_ms": per_step,
     }
+    if w.fmt == "fp8":
+        # the selective correction (VC-Attention-style, rho = 0.005): the same
+        # step with the ceil(rho N) highest-error query tokens of each head
+        # recomputed without quantization; reported beside the headline
+        rho = qs.VC_RHO
+        vws = torch.empty(qs.qsdpa_vc_workspace_bytes(params, rho), dtype=torch.uint8, device=dev)
+        for _ in range(10):
+            qs.qsdpa_forward_vc(q, k, v, out=out, workspace=vws, rho=rho, params=params, stream=stream)
+        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        v0.record(stream)
+        for _ in range(n_attn):
+            qs.qsdpa_forward_vc(q, k, v, out=out, workspace=vws, rho=rho, params=params, stream=stream)
+        v1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms_vc = v0.elapsed_time(v1) / n_attn
+        L = qs.qsdpa_vc_workspace_layout(params, rho)
+        rec["vc_forward"] = {"rho": rho, "rows_per_head": L.count, "ms_per_step": round(ms_vc, 4),
+                             "value": round(flops / (ms_vc * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                             "overhead_vs_forward": round(ms_vc / ms_step - 1.0, 4)}
     if not args.no_shapes and w.name == "kontext1024":
         # the metric's other FLUX shapes (FP8): one line each, not the headline value
         rec["shapes"] = []

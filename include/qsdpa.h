@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSDPA_ABI_VERSION 6
+#define QSDPA_ABI_VERSION 7
 #define QSDPA_HEAD_DIM 128
 
 /* Status codes (return values). */
@@ -197,6 +197,45 @@ int qsdpa_attention_bf16q(const qsdpa_params* p, const void* q, const void* work
  */
 int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o,
                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Selective correction of the FP8 path (VC-Attention-style).  The VisualGen
+ * article (FLUX 3 Image Klein Base, devotd.net, section on why the results
+ * differ) names VC-Attention FP8 with rho = 0.005 as FP8 attention that
+ * corrects only the tokens with a large error.  Reading implemented here:
+ * per (b,h), the k = ceil(rho N) query tokens whose own FP8 quantization
+ * error sum_d (q_d - code_d * s)^2 is largest (ties to the lower index) get
+ * the unquantized softmax attention of the bf16 inputs (bf16 matrix-core
+ * products with fp32 accumulation and an fp32 softmax) in place of their FP8
+ * row of O; every other row is qsdpa_forward's, bit for bit.
+ *
+ * The workspace holds qsdpa_forward's sections followed by these (byte
+ * offsets from the workspace start):
+ *   token_error: fp64 [BH][n_pad], each token's error (rows < N);
+ *   selected:    int32 [BH][count_pad], the corrected rows in ascending
+ *                order (the first `count` entries are meaningful);
+ *   partials:    fp32 scratch of the recomputation, split into `chunks`
+ *                ranges of `chunk_keys` keys.
+ * FP8 mode only (QSDPA_ERR_UNSUPPORTED otherwise); rho in (0, 1].
+ */
+typedef struct qsdpa_vc_layout {
+  uint64_t token_error, selected, partials;
+  uint64_t total;        /* workspace bytes needed (= qsdpa_vc_workspace_bytes) */
+  int32_t count;         /* k = ceil(rho N), at least 1, at most N */
+  int32_t count_pad;     /* k rounded up to 32 */
+  int32_t chunks, chunk_keys;
+} qsdpa_vc_layout;
+
+/* Workspace bytes of qsdpa_forward_vc for (p, rho), or 0 if invalid.  No GPU call. */
+size_t qsdpa_vc_workspace_bytes(const qsdpa_params* p, float rho);
+
+/* Fill *out with the layout for (p, rho).  No GPU call.  Returns a status. */
+int qsdpa_vc_workspace_layout(const qsdpa_params* p, float rho, qsdpa_vc_layout* out);
+
+/* qsdpa_forward with the selective correction: buffers as for qsdpa_forward,
+ * the workspace at least qsdpa_vc_workspace_bytes(p, rho). */
+int qsdpa_forward_vc(const qsdpa_params* p, float rho, const void* q, const void* k, const void* v, void* o,
+                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * qsdpa_forward for callers that cannot allocate device memory (code under

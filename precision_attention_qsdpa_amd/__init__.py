@@ -32,7 +32,8 @@ HEAD_DIM = 128
 
 EXPORTS = ("qsdpa_abi_version", "qsdpa_status_string", "qsdpa_validate_params", "qsdpa_workspace_bytes",
            "qsdpa_workspace_layout", "qsdpa_quantize", "qsdpa_attention", "qsdpa_forward",
-           "qsdpa_forward_noalloc", "qsdpa_attention_bf16q")
+           "qsdpa_forward_noalloc", "qsdpa_attention_bf16q", "qsdpa_vc_workspace_bytes",
+           "qsdpa_vc_workspace_layout", "qsdpa_forward_vc")
 
 
 class QsdpaParams(ctypes.Structure):
@@ -42,7 +43,7 @@ class QsdpaParams(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
-ABI_VERSION = 6   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
+ABI_VERSION = 7   # QSDPA_ABI_VERSION of include/qsdpa.h (the layout struct below)
 
 
 class QsdpaLayout(ctypes.Structure):
@@ -51,6 +52,14 @@ class QsdpaLayout(ctypes.Structure):
                                                "total")] + \
                [(n, ctypes.c_int32) for n in ("n_pad", "code_row_bytes", "q_scale_count", "k_scale_count",
                                               "stats_splits")] + [("reserved", ctypes.c_int32 * 3)]
+
+
+class QsdpaVcLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("token_error", "selected", "partials", "total")] + \
+               [(n, ctypes.c_int32) for n in ("count", "count_pad", "chunks", "chunk_keys")]
+
+
+VC_RHO = 0.005   # the fraction of tokens VC-Attention FP8 corrects on the VisualGen page
 
 
 class QsdpaError(RuntimeError):
@@ -88,6 +97,12 @@ def load() -> ctypes.CDLL:
     lib.qsdpa_attention.argtypes = [P, vp, sz, vp, vp]
     lib.qsdpa_forward.restype = ctypes.c_int
     lib.qsdpa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsdpa_vc_workspace_bytes.restype = sz
+    lib.qsdpa_vc_workspace_bytes.argtypes = [P, ctypes.c_float]
+    lib.qsdpa_vc_workspace_layout.restype = ctypes.c_int
+    lib.qsdpa_vc_workspace_layout.argtypes = [P, ctypes.c_float, ctypes.POINTER(QsdpaVcLayout)]
+    lib.qsdpa_forward_vc.restype = ctypes.c_int
+    lib.qsdpa_forward_vc.argtypes = [P, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
     lib.qsdpa_attention_bf16q.restype = ctypes.c_int
     lib.qsdpa_attention_bf16q.argtypes = [P, vp, vp, sz, vp, vp]
     lib.qsdpa_forward_noalloc.restype = ctypes.c_int
@@ -256,3 +271,47 @@ def qsdpa_forward_noalloc(q, k, v, out, params: QsdpaParams, stream=None):
     if st != QSDPA_OK:
         raise QsdpaError(st, "qsdpa_forward_noalloc")
     return out
+
+
+def qsdpa_vc_workspace_bytes(params: QsdpaParams, rho: float = VC_RHO) -> int:
+    return int(load().qsdpa_vc_workspace_bytes(ctypes.byref(params), ctypes.c_float(rho)))
+
+
+def qsdpa_vc_workspace_layout(params: QsdpaParams, rho: float = VC_RHO) -> QsdpaVcLayout:
+    out = QsdpaVcLayout()
+    st = load().qsdpa_vc_workspace_layout(ctypes.byref(params), ctypes.c_float(rho), ctypes.byref(out))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_vc_workspace_layout")
+    return out
+
+
+def qsdpa_forward_vc(q, k, v, out=None, workspace=None, *, rho: float = VC_RHO, params: QsdpaParams | None = None,
+                     stream=None):
+    """FP8 quantized SDPA with the selective correction: the ceil(rho N)
+    query tokens of each (b, h) with the largest own quantization error get
+    unquantized attention.  Returns (out, workspace); the workspace holds the
+    tokens' errors and the corrected rows (qsdpa_vc_workspace_layout)."""
+    import torch
+    if params is None:
+        B, H, N, Dh = q.shape
+        params = make_params(B, H, N, fmt="fp8", head_dim=Dh)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_qkv(t, params, n, q.device)
+    nbytes = qsdpa_vc_workspace_bytes(params, rho)
+    if nbytes == 0:
+        qsdpa_vc_workspace_layout(params, rho)   # raises with the reason
+    if out is None or workspace is None:
+        with torch.cuda.stream(_torch_stream(stream, q.device)):
+            if out is None:
+                out = torch.empty_like(q)
+            if workspace is None:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check_qkv(out, params, "out", q.device)
+    _check_workspace(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = load().qsdpa_forward_vc(ctypes.byref(params), ctypes.c_float(rho), q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != QSDPA_OK:
+        raise QsdpaError(st, "qsdpa_forward_vc")
+    return out, workspace

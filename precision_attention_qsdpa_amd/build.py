@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqsdpa.so")
-SOURCES = ["qsdpa_api.cpp", "qsdpa_quant.hip", "qsdpa_attn.hip", "qsdpa_noalloc.hip"]
+SOURCES = ["qsdpa_api.cpp", "qsdpa_quant.hip", "qsdpa_attn.hip", "qsdpa_vc.hip", "qsdpa_noalloc.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -65,6 +66,32 @@ void make_layout(const qsdpa_params* p, qsdpa_layout* L) {
   L->stats = take(bh * L->stats_splits * QSDPA_HEAD_DIM * (8 + 4));
   L->k_expanded = take(fp4 ? bh * n_pad * QSDPA_HEAD_DIM * 4 + bh * (n_pad / 64) * 4 : 0);
   L->total = off;
+}
+
+// Selective correction: rows per (b,h), their split, and the extra
+// workspace sections after the base layout.
+int vc_plan(const qsdpa_params* p, float rho, const qsdpa_layout& L, qsdpa_vc_layout* v) {
+  if (p->qk_format != QSDPA_QK_FP8_E4M3) return QSDPA_ERR_UNSUPPORTED;
+  if (!(rho > 0.f) || !(rho <= 1.f)) return QSDPA_ERR_INVALID_ARG;
+  std::memset(v, 0, sizeof(*v));
+  const int N = p->seq_len;
+  const uint64_t bh = (uint64_t)p->batch * p->heads;
+  const double want = std::ceil((double)rho * N - 1e-9);
+  v->count = (int32_t)std::min<double>(N, std::max(1.0, want));
+  v->count_pad = (v->count + 31) / 32 * 32;
+  // about 2048 waves in the recomputation, each over whole 32-key steps
+  const uint64_t groups = bh * (uint64_t)(v->count_pad / 32);
+  const int by_waves = (int)std::max<uint64_t>(1, (2048 + groups - 1) / groups);
+  const int chunks = std::min(by_waves, (N + 31) / 32);
+  v->chunk_keys = ((N + chunks - 1) / chunks + 31) / 32 * 32;
+  v->chunks = (N + v->chunk_keys - 1) / v->chunk_keys;
+  uint64_t off = L.total;
+  auto take = [&](uint64_t bytes) { const uint64_t at = off; off = align_up(off + bytes); return at; };
+  v->token_error = take(bh * L.n_pad * 8);
+  v->selected = take(bh * v->count_pad * 4);
+  v->partials = take(bh * v->count_pad * (uint64_t)v->chunks * qsdpa::VC_PART * 4);
+  v->total = off;
+  return QSDPA_OK;
 }
 
 bool aligned(const void* ptr, uint64_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -197,6 +224,66 @@ int qsdpa_attention(const qsdpa_params* p, const void* workspace, size_t ws_byte
 int qsdpa_forward(const qsdpa_params* p, const void* q, const void* k, const void* v, void* o, void* workspace,
                   size_t ws_bytes, void* stream) {
   return qsdpa::forward_impl(p, q, k, v, o, workspace, ws_bytes, stream);
+}
+
+int qsdpa_vc_workspace_layout(const qsdpa_params* p, float rho, qsdpa_vc_layout* out) {
+  int st = check_params(p);
+  if (st != QSDPA_OK) return st;
+  if (!out) return QSDPA_ERR_INVALID_ARG;
+  qsdpa_layout L;
+  make_layout(p, &L);
+  return vc_plan(p, rho, L, out);
+}
+
+size_t qsdpa_vc_workspace_bytes(const qsdpa_params* p, float rho) {
+  qsdpa_vc_layout V;
+  return qsdpa_vc_workspace_layout(p, rho, &V) == QSDPA_OK ? (size_t)V.total : 0;
+}
+
+int qsdpa_forward_vc(const qsdpa_params* p, float rho, const void* q, const void* k, const void* v, void* o,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_params(p);
+  if (st != QSDPA_OK) return st;
+  qsdpa_layout L;
+  make_layout(p, &L);
+  qsdpa_vc_layout V;
+  st = vc_plan(p, rho, L, &V);
+  if (st != QSDPA_OK) return st;
+  st = check_buffers(p, L, q, k, v, o, workspace, ws_bytes, true, true);
+  if (st != QSDPA_OK) return st;
+  if (ws_bytes < V.total) return QSDPA_ERR_WORKSPACE_TOO_SMALL;
+  const uint64_t tbytes = (uint64_t)p->batch * p->heads * p->seq_len * QSDPA_HEAD_DIM * 2;
+  if (overlaps(o, tbytes, workspace, V.total) || overlaps(q, tbytes, workspace, V.total) ||
+      overlaps(k, tbytes, workspace, V.total) || overlaps(v, tbytes, workspace, V.total))
+    return QSDPA_ERR_ALIAS;
+  (void)hipGetLastError();
+  uint8_t* w = (uint8_t*)workspace;
+  qsdpa::LaunchArgs a = make_args(p, L, q, k, v, o, workspace);
+  a.fuse_q = true;
+  a.vc_err = (double*)(w + V.token_error);
+  qsdpa::launch_quantize(a, (hipStream_t)stream);
+  if (launch_status() != QSDPA_OK) return QSDPA_ERR_HIP;
+  qsdpa::launch_attention(a, (hipStream_t)stream);
+  if (launch_status() != QSDPA_OK) return QSDPA_ERR_HIP;
+  qsdpa::VcArgs c;
+  c.batch = p->batch;
+  c.heads = p->heads;
+  c.seq_len = p->seq_len;
+  c.n_pad = L.n_pad;
+  c.count = V.count;
+  c.count_pad = V.count_pad;
+  c.chunks = V.chunks;
+  c.chunk_keys = V.chunk_keys;
+  c.softmax_scale = p->softmax_scale;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.o = o;
+  c.err = (const double*)(w + V.token_error);
+  c.sel = (int32_t*)(w + V.selected);
+  c.part = (float*)(w + V.partials);
+  qsdpa::launch_vc(c, (hipStream_t)stream);
+  return launch_status();
 }
 
 int qsdpa_attention_bf16q(const qsdpa_params* p, const void* q, const void* workspace, size_t ws_bytes, void* o,

@@ -322,7 +322,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint16_t* __restrict__ qx,
     const uint8_t* __restrict__ kc, const float* __restrict__ ks, const uint8_t* __restrict__ vc,
     const float* __restrict__ vs, uint16_t* __restrict__ out, int N, int n_pad, int block_q,
-    int q_scale_count, int k_scale_count, float tau_log2e, int tiles_per_bh, int prio_slots) {
+    int q_scale_count, int k_scale_count, float tau_log2e, int tiles_per_bh, int prio_slots,
+    double* __restrict__ vc_err) {
   set_round_priority(prio_slots);
   // ring: stages 0..3 of K tiles, then stages 0..3 of V^T tiles
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * NSTAGE * KTILE];
@@ -380,6 +381,36 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
           const int lo = cvt_e4m3x2<false>(clamp448(x[h][4 * j] * inv), clamp448(x[h][4 * j + 1] * inv), 0);
           qb8[h][j] = cvt_e4m3x2<true>(clamp448(x[h][4 * j + 2] * inv), clamp448(x[h][4 * j + 3] * inv), lo);
         }
+      if (vc_err) {
+        // the token's own quantization error sum_d (x_d - code_d * s)^2 for the
+        // selective correction: each difference is exact in fp64, the squares
+        // summed in fp64 over this lane's 64 channels, then over the lane pair
+        const double s = (double)qscale;
+        double e = 0.0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const auto c01 = __builtin_amdgcn_cvt_pk_f32_fp8(qb8[h][j], false);
+            const auto c23 = __builtin_amdgcn_cvt_pk_f32_fp8(qb8[h][j], true);
+            const double d0 = (double)x[h][4 * j] - (double)c01[0] * s;
+            const double d1 = (double)x[h][4 * j + 1] - (double)c01[1] * s;
+            const double d2 = (double)x[h][4 * j + 2] - (double)c23[0] * s;
+            const double d3 = (double)x[h][4 * j + 3] - (double)c23[1] * s;
+            e = __builtin_fma(d0, d0, e);
+            e = __builtin_fma(d1, d1, e);
+            e = __builtin_fma(d2, d2, e);
+            e = __builtin_fma(d3, d3, e);
+          }
+        // after the swap, element 0 holds the value of lane l & 31 and element
+        // 1 that of lane l | 32 (the g = 0 and g = 1 halves of the token)
+        const uint64_t eb = (uint64_t)__double_as_longlong(e);
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)eb, (uint32_t)eb, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(eb >> 32), (uint32_t)(eb >> 32), false, false);
+        const double e0 = __longlong_as_double((long long)(((uint64_t)hi[0]) << 32 | lo[0]));
+        const double e1 = __longlong_as_double((long long)(((uint64_t)hi[1]) << 32 | lo[1]));
+        if (g == 0 && q < N) vc_err[(size_t)bh * n_pad + q] = e0 + e1;
+      }
     } else {
       const uint8_t* qrow = qc + ((size_t)bh * n_pad + q0 + r) * D;
 #pragma unroll
@@ -1064,7 +1095,7 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
     auto kern = a.fuse_q ? attn_fp8_kernel<true> : attn_fp8_kernel<false>;
     kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_codes, a.k_scales,
                                     a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, a.block_q,
-                                    a.q_scale_count, a.k_scale_count, tl, tiles, slots);
+                                    a.q_scale_count, a.k_scale_count, tl, tiles, slots, a.vc_err);
   }
 }
 

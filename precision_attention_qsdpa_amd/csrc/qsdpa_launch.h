@@ -34,7 +34,27 @@ struct LaunchArgs {
   uint8_t* k_expanded;   // FP4 mode: K as f16 hi + E4M3 correction tiles
   void* stats_sum;
   void* stats_max;
+  double* vc_err = nullptr;   // FP8 with FUSE_Q: per-token Q quantization error (selective correction)
 };
+
+// Selective correction (FP8): which rows of each (b,h) are recomputed, and
+// how the recomputation is split.
+struct VcArgs {
+  int batch, heads, seq_len, n_pad;
+  int count, count_pad;   // k = ceil(rho N) rows per (b,h), and k rounded up to 32
+  int chunks, chunk_keys; // key ranges of the split recomputation
+  float softmax_scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const double* err;      // [BH][n_pad]
+  int32_t* sel;           // [BH][count_pad]
+  float* part;            // [BH][count_pad][chunks][VC_PART]
+};
+constexpr int VC_PART = 132;   // floats per partial row: m, l, 2 spare, 128 accumulators
+
+void launch_vc(const VcArgs& a, hipStream_t s);
 
 void launch_quantize(const LaunchArgs& a, hipStream_t s);
 void launch_attention(const LaunchArgs& a, hipStream_t s);

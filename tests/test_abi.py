@@ -6,6 +6,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import precision_attention_qsdpa_amd as qs
@@ -28,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 6
+    assert qs.load().qsdpa_abi_version() == qs.ABI_VERSION == 7
     for st in range(-7, 1):
         assert qs.status_string(st) not in ("", "unknown status")
     assert qs.status_string(-99) == "unknown status"
@@ -161,3 +163,26 @@ def test_noalloc_rejects_problems_beyond_the_scratch_array():
     bad = qs.make_params(1, 2, 320, block_q=96)
     assert lib.qsdpa_forward_noalloc(ctypes.byref(bad), 256, 512, 768, 1 << 40, None) == qs.QSDPA_ERR_UNSUPPORTED
     assert "static scratch" in qs.status_string(qs.QSDPA_ERR_SCRATCH_TOO_SMALL)
+
+
+def test_vc_layout_and_validation():
+    """The selective correction's plan: k = ceil(rho N) rows per (b,h) (the
+    oracle's count), padded to 32, key ranges that cover N, sections after
+    qsdpa_forward's workspace; FP8 only, rho in (0, 1]."""
+    import oracle
+    for (B, H, N, rho) in [(1, 24, 8704, 0.005), (1, 2, 320, 0.005), (2, 1, 1, 0.005), (1, 3, 1000, 1.0),
+                           (2, 24, 16896, 0.005), (1, 1, 129, 0.3)]:
+        p = qs.make_params(B, H, N, fmt="fp8")
+        L = qs.qsdpa_vc_workspace_layout(p, rho)
+        assert L.count == oracle.vc_count(N, float(np.float32(rho)))
+        assert L.count_pad % 32 == 0 and L.count <= L.count_pad < L.count + 32
+        assert L.chunk_keys % 32 == 0 and (L.chunks - 1) * L.chunk_keys < N <= L.chunks * L.chunk_keys
+        assert L.token_error >= qs.qsdpa_workspace_bytes(p) and L.token_error % 256 == 0
+        assert L.total == qs.load().qsdpa_vc_workspace_bytes(ctypes.byref(p), ctypes.c_float(rho))
+    p = qs.make_params(1, 2, 320, fmt="fp8")
+    for bad in (0.0, -0.1, 1.5, float("nan")):
+        with pytest.raises(qs.QsdpaError):
+            qs.qsdpa_vc_workspace_layout(p, bad)
+    with pytest.raises(qs.QsdpaError) as e:
+        qs.qsdpa_vc_workspace_layout(qs.make_params(1, 2, 320, fmt="mxfp4"), 0.005)
+    assert e.value.status == qs.QSDPA_ERR_UNSUPPORTED
