@@ -63,8 +63,12 @@ MAX_CPU_WORKERS = 16
 
 def _worker_init():
     """Oracle worker: single-threaded BLAS, so that the workers are the
-    parallelism."""
+    parallelism.  The thread counts are set before the worker loads NumPy's
+    BLAS (read at load time), and limited again once it is loaded."""
     global _LIMITS
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
+    import numpy  # noqa: F401  (loads BLAS with one thread)
     from threadpoolctl import threadpool_limits
     _LIMITS = threadpool_limits(limits=1)
 

@@ -78,7 +78,7 @@ def test_vc_kontext(gpu_lib):
 
 
 @pytest.mark.parametrize("N,bq,rho", [(1, 64, 0.005), (65, 64, 0.005), (129, 128, 0.1), (320, 64, 0.005),
-                                      (1000, 128, 0.05), (300, 128, 1.0), (2100, 128, 0.02)])
+                                      (1000, 128, 0.05), (300, 128, 1.0), (2100, 128, 0.02), (17000, 128, 0.005)])
 def test_vc_ragged_and_rho(gpu_lib, N, bq, rho):
     qb, kb, vb = draw(WORKLOADS["tiny"], batch=2, heads=2, seq_len=N, seed=700 + N)
     check(qb, kb, vb, bq, rho, [(0, 0), (1, 1)], f"N={N} rho={rho}")
