@@ -13,7 +13,8 @@
  * tokens (same articles).  They print no formula; the steps below are the
  * reading this library implements:
  *
- *   1. per (b,h,d): mu = fp32(sum_n K / N) (sum in fp64), vmax = max_n |V|;
+ *   1. per (b,h,d): mu = fp32(fp64(sum_n K) / N), the exact sum rounded once
+ *      to fp64 (for every finite input), vmax = max_n |V|;
  *   2. Ks = fp32(K - mu) (K smoothing: softmax is unchanged by it);
  *   3. FP8 mode: Q per block of block_q tokens, Ks per block of block_k
  *      tokens, scale s = fp32(amax/448), code = E4M3(fp32(x * fp32(448/amax)));
@@ -117,7 +118,9 @@ typedef struct qsdpa_params {
  *                     with g = p>>5, kb = (p>>4)&1, r = p&15.
  *   v_scales:         fp32 [BH][128] (sV).
  *   v_amax:           fp32 [BH][128] (vmax).
- *   stats:            scratch for partial channel sums (fp64) and maxima.
+ *   stats:            scratch for the statistics pass, per token range of
+ *                     256 and channel: fp64 sums of K, fp32 maxima of |V|,
+ *                     and the largest and smallest nonzero |K| (bf16 bits).
  *   k_expanded:       FP4 mode only (0 bytes in other modes): every K
  *                     element x = code * scale (one fp32 product) times
  *                     2^-E of its 64-key tile, x', as hi = f16(x') and the

@@ -34,6 +34,7 @@ struct LaunchArgs {
   uint8_t* k_expanded;   // FP4 mode: K as f16 hi + E4M3 correction tiles
   void* stats_sum;
   void* stats_max;
+  void* stats_range;
   double* vc_err = nullptr;   // FP8 with FUSE_Q: per-token Q quantization error (selective correction)
 };
 

@@ -26,20 +26,30 @@ __device__ __forceinline__ int last_first(int y) { return (int)gridDim.y - 1 - y
 
 // ---------------------------------------------------------------------------
 // Channel statistics, pass 1: per (b,h, token range of STATS_ROWS tokens)
-// partial fp64 sums of K and fp32 maxima of |V| over the range.
+// partial fp64 sums of K, fp32 maxima of |V|, and the range of K's
+// magnitudes: the largest |K| and the smallest nonzero |K|, as bf16 bits
+// (max in the high half of a word, min - 1 in the low half; 0xffff when the
+// range has no nonzero K).  The magnitudes are tracked two channels at a
+// time with packed 16-bit integer operations: bf16 magnitudes order like
+// their bit patterns, and min - 1 wraps a zero to 0xffff.
 // grid = (splits, BH), block = 256: thread = (row lane 0..15, 8 channels).
 // ---------------------------------------------------------------------------
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(256) void stats_partial_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int splits,
-    double* __restrict__ psum, float* __restrict__ pmax) {
+    double* __restrict__ psum, float* __restrict__ pmax, uint32_t* __restrict__ prange) {
   const int split = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, cg = tid & 15, rl = tid >> 4;
   const size_t base = (size_t)bh * N * D + cg * 8;
   const int n0 = split * STATS_ROWS, n1 = min(N, n0 + STATS_ROWS);
   double s[8];
   float m[8];
+  u16x2 kmx[4], kmn[4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) { s[j] = 0.0; m[j] = 0.f; }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { kmx[j] = u16x2{0, 0}; kmn[j] = u16x2{0xffff, 0xffff}; }
   for (int n = n0 + rl; n < n1; n += 16) {
     const u32x4 kk = *(const u32x4*)(k + base + (size_t)n * D);
     const u32x4 vv = *(const u32x4*)(v + base + (size_t)n * D);
@@ -49,46 +59,173 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
       s[2 * j + 1] += (double)bf16_hi(kk[j]);
       m[2 * j] = fmaxf(m[2 * j], fabsf(bf16_lo(vv[j])));
       m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(bf16_hi(vv[j])));
+      const u16x2 mag = __builtin_bit_cast(u16x2, kk[j] & 0x7fff7fffu);
+      kmx[j] = __builtin_elementwise_max(kmx[j], mag);
+      kmn[j] = __builtin_elementwise_min(kmn[j], mag - u16x2{1, 1});
     }
   }
   __shared__ double lsum[16][D];
   __shared__ float lmax[16][D];
+  __shared__ uint32_t lrange[16][D];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { lsum[rl][cg * 8 + j] = s[j]; lmax[rl][cg * 8 + j] = m[j]; }
+  for (int j = 0; j < 8; ++j) {
+    lsum[rl][cg * 8 + j] = s[j];
+    lmax[rl][cg * 8 + j] = m[j];
+    lrange[rl][cg * 8 + j] = (uint32_t)kmx[j >> 1][j & 1] << 16 | kmn[j >> 1][j & 1];
+  }
   __syncthreads();
   if (tid < D) {
     double t = 0.0;
     float mm = 0.f;
-    for (int r = 0; r < 16; ++r) { t += lsum[r][tid]; mm = fmaxf(mm, lmax[r][tid]); }
-    psum[((size_t)bh * splits + split) * D + tid] = t;
-    pmax[((size_t)bh * splits + split) * D + tid] = mm;
+    uint32_t hi = 0, lo = 0xffff;
+    for (int r = 0; r < 16; ++r) {
+      t += lsum[r][tid];
+      mm = fmaxf(mm, lmax[r][tid]);
+      hi = max(hi, lrange[r][tid] >> 16);
+      lo = min(lo, lrange[r][tid] & 0xffffu);
+    }
+    const size_t at = ((size_t)bh * splits + split) * D + tid;
+    psum[at] = t;
+    pmax[at] = mm;
+    prange[at] = hi << 16 | lo;
   }
+}
+
+// The exact sum of one channel of K over the tokens of a (b,h), rounded once
+// to fp64 (nearest, ties to even), for channels whose values span too many
+// binades for fp64 partial sums to be exact.  Every bf16 value is an integer
+// M < 256 times 2^(p - 133), p = max(exponent field, 1) - 1 in 0..253, so the
+// sum is an integer times 2^-133 below 2^(254 + 8 + 22): each thread adds
+// +-M << (p % 32) into the int64 digit p / 32 (8 digits of 32 bits with
+// headroom), the block adds the digits, and one thread carries them into
+// 32-bit limbs of a two's complement integer and rounds its magnitude's top
+// 53 bits with the bits below.  N <= 2^22 keeps every digit sum below 2^62.
+// Called by all threads of a 128-thread block; returns the sum to all.
+__device__ double exact_channel_sum(const uint16_t* __restrict__ kcol, int N, long long (*part)[128],
+                                    long long* tot, uint32_t* limb, double* result) {
+  const int tid = threadIdx.x;
+  long long acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0;
+  for (int n = tid; n < N; n += 128) {
+    const uint32_t h = kcol[(size_t)n * D];
+    const uint32_t f = (h >> 7) & 0xffu, man = h & 0x7fu;
+    const long long M = (long long)(f ? (man | 0x80u) : man);
+    const int p = (int)max(f, 1u) - 1;
+    const long long t = M << (p & 31);
+    const long long st = (h & 0x8000u) ? -t : t;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += (p >> 5) == j ? st : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) part[j][tid] = acc[j];
+  __syncthreads();
+  if (tid < 8) {
+    long long x = 0;
+    for (int i = 0; i < 128; ++i) x += part[tid][i];
+    tot[tid] = x;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // carry into 10 limbs of 32 bits (two's complement), then the magnitude
+    long long c = 0;
+    for (int j = 0; j < 8; ++j) {
+      const long long x = tot[j] + c;
+      limb[j] = (uint32_t)x;
+      c = x >> 32;   // arithmetic: floor division by 2^32
+    }
+    limb[8] = (uint32_t)c;
+    limb[9] = (uint32_t)(c >> 32);
+    const bool neg = (int32_t)limb[9] < 0;
+    if (neg) {
+      uint32_t carry = 1;
+      for (int j = 0; j < 10; ++j) {
+        const uint64_t x = (uint64_t)(~limb[j]) + carry;
+        limb[j] = (uint32_t)x;
+        carry = (uint32_t)(x >> 32);
+      }
+    }
+    auto bit = [&](int i) -> uint64_t { return (limb[i >> 5] >> (i & 31)) & 1u; };
+    int top = -1;
+    for (int i = 319; i >= 0 && top < 0; --i)
+      if (bit(i)) top = i;
+    double r = 0.0;
+    if (top >= 0) {
+      const int lo = max(top - 52, 0);
+      uint64_t mant = 0;
+      for (int i = top; i >= lo; --i) mant = mant << 1 | bit(i);
+      if (lo > 0) {
+        uint64_t sticky = 0;
+        for (int i = 0; i < lo - 1; ++i) sticky |= bit(i);
+        if (bit(lo - 1) && (sticky || (mant & 1u))) ++mant;   // at most 2^53: exact in fp64
+      }
+      r = ldexp((double)mant, lo - 133);
+      if (neg) r = -r;
+    }
+    *result = r;
+  }
+  __syncthreads();
+  const double r = *result;
+  __syncthreads();   // the shared buffers are reused by the next call
+  return r;
 }
 
 // Pass 2: per (b,h), combine the ranges: mu = fp32(fp64 sum / N),
 // vmax = max, sV = fp32(vmax / 448).  grid = BH, block = 128 (one channel each).
 // The partial sums are fetched eight at a time (independent loads) and added
-// in range order.
+// in range order.  That sum is exact, in any order, when every value is a
+// multiple of the smallest nonzero one's unit in the last place and N times
+// the largest stays within 53 bits of it: with exponent fields e_hi of the
+// largest and e_lo (at least 1) of the smallest, e_hi - e_lo + ceil(log2 N)
+// <= 45.  A channel beyond that (and with a finite sum) is summed again by
+// exact_channel_sum from K itself.
 __global__ __launch_bounds__(128) void stats_final_kernel(
-    const double* __restrict__ psum, const float* __restrict__ pmax, int N, int splits,
-    float* __restrict__ mu, float* __restrict__ vamax, float* __restrict__ vscale) {
+    const double* __restrict__ psum, const float* __restrict__ pmax, const uint32_t* __restrict__ prange,
+    const uint16_t* __restrict__ k, int N, int splits, float* __restrict__ mu, float* __restrict__ vamax,
+    float* __restrict__ vscale) {
   const int bh = blockIdx.x, d = threadIdx.x;
   const double* ps = psum + (size_t)bh * splits * D + d;
   const float* pm = pmax + (size_t)bh * splits * D + d;
+  const uint32_t* pr = prange + (size_t)bh * splits * D + d;
   double t = 0.0;
   float mm = 0.f;
+  uint32_t hi = 0, lo = 0xffff;
   int s = 0;
   for (; s + 8 <= splits; s += 8) {
     double x[8];
     float y[8];
+    uint32_t z[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { x[i] = ps[(s + i) * D]; y[i] = pm[(s + i) * D]; }
+    for (int i = 0; i < 8; ++i) { x[i] = ps[(s + i) * D]; y[i] = pm[(s + i) * D]; z[i] = pr[(s + i) * D]; }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { t += x[i]; mm = fmaxf(mm, y[i]); }
+    for (int i = 0; i < 8; ++i) {
+      t += x[i];
+      mm = fmaxf(mm, y[i]);
+      hi = max(hi, z[i] >> 16);
+      lo = min(lo, z[i] & 0xffffu);
+    }
   }
   for (; s < splits; ++s) {
     t += ps[s * D];
     mm = fmaxf(mm, pm[s * D]);
+    hi = max(hi, pr[s * D] >> 16);
+    lo = min(lo, pr[s * D] & 0xffffu);
+  }
+  const int log2n = N > 1 ? 32 - __clz(N - 1) : 0;
+  const int e_hi = (int)(hi >> 7), e_lo = max((int)((lo + 1) >> 7), 1);
+  const bool inexact = lo != 0xffffu && e_hi - e_lo + log2n > 45 && isfinite(t);
+  __shared__ int redo[D];
+  redo[d] = inexact;
+  if (__syncthreads_or(inexact)) {
+    __shared__ long long part[8][128];
+    __shared__ long long tot[8];
+    __shared__ uint32_t limb[10];
+    __shared__ double result;
+    for (int c = 0; c < D; ++c) {
+      if (!redo[c]) continue;   // uniform: every thread reads the same word
+      const double x = exact_channel_sum(k + (size_t)bh * N * D + c, N, part, tot, limb, &result);
+      if (d == c) t = x;
+    }
   }
   mu[bh * D + d] = (float)(t / (double)N);
   vamax[bh * D + d] = mm;
@@ -464,9 +601,10 @@ void launch_quantize(const LaunchArgs& a, hipStream_t s) {
   const int BH = a.batch * a.heads;
   stats_partial_kernel<<<dim3(a.stats_splits, BH), 256, 0, s>>>(
       (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_len, a.stats_splits, (double*)a.stats_sum,
-      (float*)a.stats_max);
+      (float*)a.stats_max, (uint32_t*)a.stats_range);
   stats_final_kernel<<<BH, 128, 0, s>>>((const double*)a.stats_sum, (const float*)a.stats_max,
-                                        a.seq_len, a.stats_splits, a.k_mean, a.v_amax, a.v_scales);
+                                        (const uint32_t*)a.stats_range, (const uint16_t*)a.k, a.seq_len,
+                                        a.stats_splits, a.k_mean, a.v_amax, a.v_scales);
   const int vtiles = a.n_pad / KSTEP;
   if (a.mx) {
     // Q blocks skipped when the attention kernel quantizes Q

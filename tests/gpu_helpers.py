@@ -142,3 +142,47 @@ def tiny_magnitude_inputs(N: int = 300, seed: int = 31):
     v[..., 5] *= np.float32(4e-39)
     v[..., 6] = 0
     return to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v)
+
+
+def wide_span_inputs(N: int = 1000, seed: int = 11):
+    """bf16 bit patterns of Q, K, V [1, 2, N, 128] (N >= 800) whose K channels
+    0..4 span far more binades than an fp64 sum can hold exactly: channel 0
+    has +-2^60 at two tokens that cancel (head 0: tokens 5 and 250, one range
+    of 256 tokens; head 1: tokens 3 and 700, two ranges), channel 1 one token
+    of 2^100, channel 2 bf16 subnormals on every other token, channel 3
+    opposite pairs +-x with x from 2^-100 to 2^100, channel 4 +-2^40 on every
+    16th token; the other channels and Q, V are N(0, 1)."""
+    from workloads import WORKLOADS, draw
+    qb, kb, vb = draw(WORKLOADS["tiny"], seq_len=N, seed=seed)
+    kb = kb.copy()
+    rng = np.random.default_rng(seed)
+    big = lambda e: np.uint16(0x3F80 + (e << 7))          # bf16 bits of 2^e
+    for h, (i, j) in enumerate([(5, 250), (3, 700)]):
+        kb[0, h, i, 0] = big(60)
+        kb[0, h, j, 0] = big(60) | np.uint16(0x8000)
+        kb[0, h, 17 + h, 1] = big(100)
+        kb[0, h, ::2, 2] = rng.integers(1, 128, len(kb[0, h, ::2, 2])).astype(np.uint16)
+        half = N // 2
+        e = rng.integers(-100, 101, half)
+        x = (big(0) + (e << 7).astype(np.int32) + rng.integers(0, 128, half)).astype(np.uint16)
+        kb[0, h, :half, 3] = x
+        kb[0, h, half:2 * half, 3] = x ^ np.uint16(0x8000)
+        kb[0, h, ::16, 4] = big(40) | (rng.integers(0, 2, len(kb[0, h, ::16, 4])) << 15).astype(np.uint16)
+    return qb, kb, vb
+
+
+def fixed_order_fp64_sum(col: np.ndarray) -> float:
+    """fp64 sum of one K channel (bf16 bits, N tokens) in a fixed blocked
+    order: within each range of 256 tokens, 16 running sums over the tokens
+    r, r + 16, ... (r = 0..15), added in r order; then the ranges in order."""
+    x = (col.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    total = 0.0
+    for s in range(0, len(x), 256):
+        part = 0.0
+        for r in range(16):
+            acc = 0.0
+            for v in x[s + r:s + 256:16]:
+                acc += v
+            part += acc
+        total += part
+    return total

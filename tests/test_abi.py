@@ -95,7 +95,7 @@ def test_workspace_closed_form(B, H, N, fmt, bq):
     ksc = {"fp8": npad // 64, "fp4": npad * 8, "mxfp4": npad * 4}[fmt]
     sb = 1 if fmt == "mxfp4" else 4
     sizes = [BH * npad * crb, BH * npad * crb, BH * npad * 128, BH * qsc * sb, BH * ksc * sb,
-             BH * 512, BH * 512, BH * 512, BH * splits * 128 * 12,
+             BH * 512, BH * 512, BH * 512, BH * splits * 128 * 16,
              BH * npad * 128 * 4 + BH * (npad // 64) * 4 if fmt == "fp4" else 0]
     assert (L.n_pad, L.code_row_bytes, L.q_scale_count, L.k_scale_count, L.stats_splits) == (npad, crb, qsc, ksc, splits)
     assert L.total == sum(_round(s, 256) for s in sizes)

@@ -140,3 +140,20 @@ def test_quantize_e2m1_ties(gpu_lib, fmt):
     kb = np.concatenate([kh, kh ^ np.uint16(0x8000)]).reshape(1, 1, N, 128)
     _, _, vb = draw(WORKLOADS["tiny"], heads=1, seq_len=N, seed=9)
     check_quantize(qb, kb, vb, fmt, 128, [(0, 0)], f"ties-{fmt}")
+
+
+@pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp4", 128), ("mxfp4", 128)])
+def test_quantize_k_mean_exact_beyond_fp64_range(gpu_lib, fmt, bq):
+    """K channels whose values span more binades than fp64 partial sums hold
+    (so a blocked fp64 sum drops low bits or cancels the wrong way): the
+    channel mean is still fp32(fp64(exact sum) / N), bit for bit."""
+    import math
+    from gpu_helpers import fixed_order_fp64_sum, wide_span_inputs
+    qb, kb, vb = wide_span_inputs()
+    N = qb.shape[2]
+    for h in range(2):
+        exact = math.fsum(oracle.bf16_bits_to_f64(kb[0, h, :, 0]))
+        # a blocked fp64 sum of channel 0 loses the small values beside +-2^60
+        assert fixed_order_fp64_sum(kb[0, h, :, 0]) != exact
+        assert np.float32(fixed_order_fp64_sum(kb[0, h, :, 0]) / N) != np.float32(exact / N)
+    check_quantize(qb, kb, vb, fmt, bq, [(0, 0), (0, 1)], f"wide-span-{fmt}")
