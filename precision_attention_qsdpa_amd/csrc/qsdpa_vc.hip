@@ -56,6 +56,7 @@ __global__ __launch_bounds__(VC_SEL) void vc_select_kernel(const double* __restr
   __shared__ int s_need;
   __shared__ int wsum[VC_SEL_WAVES];
   __shared__ int s_last;
+  __shared__ int s_done;
   const int per = (N + VC_SEL - 1) / VC_SEL, i0 = min(N, tid * per), n_run = min(N, i0 + per) - i0;
   uint64_t kr[IN_REGS ? VC_RUN : 1];
   if constexpr (IN_REGS) {
@@ -73,7 +74,10 @@ __global__ __launch_bounds__(VC_SEL) void vc_select_kernel(const double* __restr
     }
   };
   // the k-th largest key T, one byte per pass from the top; need = how many
-  // keys equal to T are taken (the rest of the k are the keys above T)
+  // keys equal to T are taken (the rest of the k are the keys above T).  The
+  // passes stop early once every key under the bytes found so far is taken:
+  // T is then that prefix (mask covers its bytes), and the comparisons below
+  // are on the masked keys.
   uint64_t prefix = 0, mask = 0;
   int need = count;
   for (int shift = 56; shift >= 0; shift -= 8) {
@@ -108,26 +112,28 @@ __global__ __launch_bounds__(VC_SEL) void vc_select_kernel(const double* __restr
     if (tid == first) {
       s_prefix = prefix | ((uint64_t)(255 - tid) << shift);
       s_need = need - (cum - h);
+      s_done = need - (cum - h) == h;
     }
     __syncthreads();
     prefix = s_prefix;
     need = s_need;
     mask |= (uint64_t)0xff << shift;
+    if (s_done) break;   // uniform: every thread reads the same word after the barrier
   }
   // rows in ascending order: every key above T, and the first `need` keys
   // equal to T; each run's place from block-wide prefix counts
   int gt_c = 0, eq_c = 0;
   visit([&](int, uint64_t u) {
-    gt_c += u > prefix;
-    eq_c += u == prefix;
+    gt_c += (u & mask) > prefix;
+    eq_c += (u & mask) == prefix;
   });
   const int eq_before = block_scan(eq_c, wtot) - eq_c;
   const int take_c = gt_c + min(eq_c, max(0, need - eq_before));
   int pos = block_scan(take_c, wtot) - take_c;
   int eq_seen = eq_before;
   visit([&](int u, uint64_t x) {
-    bool take = x > prefix;
-    if (x == prefix) take = eq_seen++ < need;
+    bool take = (x & mask) > prefix;
+    if ((x & mask) == prefix) take = eq_seen++ < need;
     if (take) {
       sel[(size_t)bh * count_pad + pos] = i0 + u;
       if (pos == count - 1) s_last = i0 + u;
@@ -156,8 +162,8 @@ constexpr int VC_WAVES = 2;
 
 __global__ __launch_bounds__(64 * VC_WAVES) void vc_partial_kernel(
     const uint16_t* __restrict__ qx, const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx,
-    const int32_t* __restrict__ sel, float* __restrict__ part, int N, int count_pad, int chunks, int chunk_keys,
-    float tau_log2e) {
+    const int32_t* __restrict__ sel, float* __restrict__ part, int N, int count, int count_pad, int chunks,
+    int chunk_keys, float tau_log2e) {
   const int qgroups = count_pad / 32, qblocks = (qgroups + VC_WAVES - 1) / VC_WAVES;
   const int c = blockIdx.x % chunks, rest = blockIdx.x / chunks;
   const int qb = rest % qblocks, bh = rest / qblocks;
@@ -286,6 +292,8 @@ __global__ __launch_bounds__(64 * VC_WAVES) void vc_partial_kernel(
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
     lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
+  // padding rows (repeats of the last selected row) are not combined
+  if (32 * qg + r >= count) return;
   // O^T column r: channels 32 db + 4g + 8j + (0..3) in registers 4j .. 4j + 3
   float* dst = part + (((size_t)bh * count_pad + 32 * qg + r) * chunks + c) * VC_PART;
   if (g == 0) {
@@ -301,25 +309,58 @@ __global__ __launch_bounds__(64 * VC_WAVES) void vc_partial_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Combine.  grid = BH * count, block = 128 (one channel each).
+// Combine.  grid = BH * count, block = 64 (one wave per corrected row): lane
+// l takes channels 8 (l % 16) .. + 7 of the ranges c = l / 16, l / 16 + 4,
+// ..., merges them online (running max, rescaled sum and accumulators), and
+// the four lanes of a channel group merge their results through shuffles.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void vc_combine_kernel(const int32_t* __restrict__ sel, const float* __restrict__ part,
-                                                          uint16_t* __restrict__ out, int N, int count, int count_pad,
-                                                          int chunks) {
-  const int bh = blockIdx.x / count, j = blockIdx.x % count, d = threadIdx.x;
+__global__ __launch_bounds__(64) void vc_combine_kernel(const int32_t* __restrict__ sel, const float* __restrict__ part,
+                                                         uint16_t* __restrict__ out, int N, int count, int count_pad,
+                                                         int chunks) {
+  const int bh = blockIdx.x / count, j = blockIdx.x % count, lane = threadIdx.x, cl = lane >> 4, cg = lane & 15;
   const float* src = part + ((size_t)bh * count_pad + j) * chunks * VC_PART;
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < chunks; ++c) M = fmaxf(M, src[c * VC_PART]);
-  float L = 0.f, acc = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < chunks; ++c) {
-    const float w = __builtin_amdgcn_exp2f(src[c * VC_PART] - M);
-    L += w * src[c * VC_PART + 1];
-    acc += w * src[c * VC_PART + 4 + d];
+  float M = -INFINITY, L = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int c = cl; c < chunks; c += 4) {
+    const float* p = src + (size_t)c * VC_PART;
+    const float mc = p[0], lc = p[1];
+    const float4 x0 = *(const float4*)(p + 4 + 8 * cg), x1 = *(const float4*)(p + 8 + 8 * cg);
+    const float Mn = fmaxf(M, mc);
+    const float a = __builtin_amdgcn_exp2f(M - Mn), w = __builtin_amdgcn_exp2f(mc - Mn);
+    L = a * L + w * lc;
+    acc[0] = a * acc[0] + w * x0.x;
+    acc[1] = a * acc[1] + w * x0.y;
+    acc[2] = a * acc[2] + w * x0.z;
+    acc[3] = a * acc[3] + w * x0.w;
+    acc[4] = a * acc[4] + w * x1.x;
+    acc[5] = a * acc[5] + w * x1.y;
+    acc[6] = a * acc[6] + w * x1.z;
+    acc[7] = a * acc[7] + w * x1.w;
+    M = Mn;
   }
-  const int row = sel[(size_t)bh * count_pad + j];
-  out[((size_t)bh * N + row) * D + d] = (uint16_t)f32_to_bf16(acc / L);
+  // merge the four chunk lanes of each channel group (lanes cg, cg + 16, cg + 32, cg + 48)
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    const float Mo = __shfl_xor(M, o), Lo = __shfl_xor(L, o);
+    const float Mn = fmaxf(M, Mo);
+    // a lane with no ranges has M = -inf; exp2(-inf - Mn) = 0 drops it
+    const float a = Mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float b = Mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mo - Mn);
+    L = a * L + b * Lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = a * acc[e] + b * __shfl_xor(acc[e], o);
+    M = Mn;
+  }
+  if (cl == 0) {
+    const int row = sel[(size_t)bh * count_pad + j];
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = f32_to_bf16(acc[2 * e] / L) | (uint32_t)f32_to_bf16(acc[2 * e + 1] / L) << 16;
+    *(u32x4*)(out + ((size_t)bh * N + row) * D + 8 * cg) = w;
+  }
 }
 
 void launch_vc(const VcArgs& a, hipStream_t s) {
@@ -328,10 +369,10 @@ void launch_vc(const VcArgs& a, hipStream_t s) {
   select<<<BH, VC_SEL, 0, s>>>(a.err, a.sel, a.seq_len, a.n_pad, a.count, a.count_pad);
   const int qblocks = (a.count_pad / 32 + VC_WAVES - 1) / VC_WAVES;
   vc_partial_kernel<<<BH * qblocks * a.chunks, 64 * VC_WAVES, 0, s>>>(
-      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.sel, a.part, a.seq_len, a.count_pad,
-      a.chunks, a.chunk_keys, a.softmax_scale * LOG2E);
-  vc_combine_kernel<<<BH * a.count, 128, 0, s>>>(a.sel, a.part, (uint16_t*)a.o, a.seq_len, a.count, a.count_pad,
-                                                a.chunks);
+      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.sel, a.part, a.seq_len, a.count,
+      a.count_pad, a.chunks, a.chunk_keys, a.softmax_scale * LOG2E);
+  vc_combine_kernel<<<BH * a.count, 64, 0, s>>>(a.sel, a.part, (uint16_t*)a.o, a.seq_len, a.count, a.count_pad,
+                                               a.chunks);
 }
 
 }  // namespace qsdpa
