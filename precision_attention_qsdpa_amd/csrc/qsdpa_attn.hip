@@ -47,6 +47,7 @@ namespace qsdpa {
 constexpr int WAVES = 4;
 constexpr int QW = 32;              // queries per wave
 constexpr int QT = QW * WAVES;      // queries per workgroup
+constexpr int FP4_WAVES = 8, FP4_T = 64 * FP4_WAVES;   // FP4 kernel: two groups of four waves
 constexpr int KTILE = KSTEP * D;    // bytes of an FP8 K tile / V^T tile
 
 // LDS byte offset of 16-byte chunk c of row `row` in an FP8 K tile (128-B rows).
@@ -828,11 +829,13 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
 // f16 and E4M3 value in range; the softmax constant tau * log2(e) *
 // 2^(EQ + EK) of the lane and step takes both back.  P and V stay FP8.
 // The tiles reach LDS as in the FP8 kernel, by asynchronous copies
-// (global_load_lds_dwordx4), through a ring of 2 stages of 32 KB K + 8 KB V^T:
-// 80 KB, so that two workgroups share a CU and two waves share each SIMD.
-// The Q operands take 64 registers, so a wave has one scores buffer: its
-// softmax and its MFMAs alternate, and the other wave of the SIMD fills the
-// gaps.
+// (global_load_lds_dwordx4), through a ring of 2 stages of 32 KB K + 8 KB V^T
+// (80 KB).  The Q operands take 64 registers, so a wave has one scores
+// buffer: its softmax and its MFMAs alternate.  A workgroup is 8 waves, 256
+// queries, one per CU: two groups of four waves, the second running one
+// half-step behind the first, so that the two waves of each SIMD alternate
+// between softmax and MFMAs; the eight waves share each K/V tile, which
+// halves the tile copies per query against two 4-wave workgroups per CU.
 // ---------------------------------------------------------------------------
 // FUSE_Q: Q arrives as bf16 (qx), and each lane makes the codes and fp32
 // scales of the 8 sixteen-channel groups of its query with the quantize
@@ -840,14 +843,13 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
 // product, clamp, E2M1 conversion), so the result is bit-identical to reading
 // the pass's codes (qc, qs).  Both lanes of a query make all 8 groups.
 template <bool FUSE_Q>
-__global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
+__global__ __launch_bounds__(FP4_T, 1) void attn_fp4_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qs, const uint16_t* __restrict__ qx,
     const uint8_t* __restrict__ kx, const int* __restrict__ kexp, const uint8_t* __restrict__ vc,
     const float* __restrict__ vs, uint16_t* __restrict__ out, int N, int n_pad, float tau_log2e,
-    int tiles_per_bh, int prio_slots) {
-  set_round_priority(prio_slots);
+    int tiles_per_bh) {
   // ring: stages 0, 1 of expanded K tiles (f16 hi, then E4M3 corrections), then stages 0, 1
-  // of V^T tiles: 80 KB, so that two workgroups share a CU's 160 KB
+  // of V^T tiles: 80 KB
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * (KXTILE + KTILE)];
   auto lds_k = [&](int S) -> uint8_t* { return ring + S * KXTILE; };
   auto lds_v = [&](int S) -> uint8_t* { return ring + 2 * KXTILE + S * KTILE; };
@@ -857,7 +859,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / tiles_per_bh, tile = wg - bh * tiles_per_bh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
-  const int q0 = tile * QT + wave * QW;
+  const int q0 = tile * (FP4_WAVES * QW) + wave * QW;
+  const bool grp_b = wave >= FP4_WAVES / 2;   // the group one slot behind
   const int T = (N + KSTEP - 1) / KSTEP;
 
   // Q operands of query q0 + r, scaled by 2^-EQ of the query row (both lanes
@@ -902,8 +905,13 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
         cw[c][0] = live ? e2m1_word8(val, inv) : 0u;
         cw[c][1] = live ? e2m1_word8(val + 8, inv) : 0u;
       } else {
-        sc[c] = qs[qrow * 8 + c];
-        const u32x2 w = *(const u32x2*)(qc + qrow * 64 + 8 * c);
+        // rows at or past n_pad (the second half of a head's last query tile) read as zero
+        u32x2 w = {0u, 0u};
+        sc[c] = 0.f;
+        if (q0 + r < n_pad) {
+          sc[c] = qs[qrow * 8 + c];
+          w = *(const u32x2*)(qc + qrow * 64 + 8 * c);
+        }
         cw[c][0] = w[0];
         cw[c][1] = w[1];
       }
@@ -952,28 +960,25 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
   const int voff0 = v_off(r, 2 * g), voff1 = v_off(r, 2 * g + 1);
 
   // Ring copies.  An expanded K tile is already in LDS order: wave w copies
-  // its 1 KB pieces 8w .. 8w+7 unchanged.  V^T tiles as in the FP8 kernel:
-  // wave w's instruction i fills LDS chunks (2w+i)*64 + lane of a stage with
-  // the global chunk the swizzle puts there.
+  // its 1 KB pieces 4w .. 4w+3 unchanged.  V^T tiles as in the FP8 kernel:
+  // wave w fills LDS chunks w*64 + lane of a stage with the global chunk the
+  // swizzle puts there.
   const uint32_t kgl = (uint32_t)lane * 16u;
-  uint32_t vg[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int P = (2 * wave + i) * 64 + lane;
+  uint32_t vg;
+  {
+    const int P = wave * 64 + lane;
     const int d = P >> 2, pv = P & 3;
-    vg[i] = (uint32_t)(d * 64 + ((pv ^ ((d >> 2) & 3)) << 4));
+    vg = (uint32_t)(d * 64 + ((pv ^ ((d >> 2) & 3)) << 4));
   }
   auto ring_k = [&](int t, int S) {
-    const uint8_t* tp = kxbase + (size_t)t * KXTILE + wave_u * 8192u;
-    const uint32_t dst = ring_lds + (uint32_t)S * KXTILE + wave_u * 8192u;
+    const uint8_t* tp = kxbase + (size_t)t * KXTILE + wave_u * 4096u;
+    const uint32_t dst = ring_lds + (uint32_t)S * KXTILE + wave_u * 4096u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ring_copy16(tp + i * 1024, kgl, dst + i * 1024);
+    for (int i = 0; i < 4; ++i) ring_copy16(tp + i * 1024, kgl, dst + i * 1024);
   };
   auto ring_v = [&](int t, int S) {
     const uint8_t* tp = vbase + (size_t)t * KTILE;
-    const uint32_t dst = ring_lds + 2 * KXTILE + (uint32_t)S * KTILE + wave_u * 2048u;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) ring_copy16(tp, vg[i], dst + i * 1024);
+    ring_copy16(tp, vg, ring_lds + 2 * KXTILE + (uint32_t)S * KTILE + wave_u * 1024u);
   };
 
   // scores of a 64-key tile: the chains of keys 0..31 and 32..63 interleaved;
@@ -1012,50 +1017,68 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(
   float m = -INFINITY, l = 0.f;
 
   // Prologue: K(0), K(1), V(0) land (after the Q loads, so that from here on
-  // the only vector-memory loads in flight are ring copies), then the scores
-  // of step 0; the second barrier lets step 0 refill K stage 0.
+  // the only vector-memory loads in flight are ring copies), then group A
+  // makes the scores of step 0.
   const int Tm1 = T - 1;
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
   ring_k(0, 0);
-  ring_k(min(1, Tm1), 1);
+  if (T > 1) ring_k(1, 1);
   ring_v(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0070);
   asm volatile("s_barrier" ::: "memory");
   v16f s[2];
-  scores(lds_k(0), s);
+  v8i pb = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  float alpha;
   int ken = kebase[0];
+  if (!grp_b) scores(lds_k(0), s);
   ring_stress(-1, 1);
-  __builtin_amdgcn_s_waitcnt(0x0070);
-  asm volatile("s_barrier" ::: "memory");
+  auto softmax = [&](int t) {
+    const float c = ldexpf(cq, ken);
+    pb = (t + 1) * KSTEP <= N ? softmax_step<true>(s, c, m, l, alpha, t * KSTEP, N, g)
+                              : softmax_step<false>(s, c, m, l, alpha, t * KSTEP, N, g);
+    rescale_o(o, alpha);
+  };
 
-  // Step t (S = t & 1): issue K(t+2) into K stage S (K(t) was read in step
-  // t-1) and V(t+1) into V stage S^1 (V(t-1) was read in step t-1); softmax of
-  // S(t); O = alpha O + V(t) P(t); scores S(t+1) from K stage S^1.  The
-  // copies have the whole step to land: at its end every copy is waited for,
-  // and the barrier hands the stages over.  One scores buffer: the two waves
-  // of a SIMD (two workgroups per CU) overlap one's softmax with the other's
-  // MFMAs.
+  // Slots, each closed by a barrier of all eight waves.  Group A (waves 0-3)
+  // runs the softmax of step t in slot 2t and the MFMAs of step t (values of
+  // t, scores of t+1) in slot 2t+1; group B (waves 4-7, one per SIMD beside
+  // a wave of group A) runs the same sequence one slot later, so that each
+  // SIMD overlaps one wave's softmax with the other's MFMAs.
+  // K(t) is read in slots 2t-1 (A) and 2t (B), V(t) in slots 2t+1 (A) and
+  // 2t+2 (B).  Slot 2t+1 copies K(t+2) over K(t) and V(t+1) over V(t-1); the
+  // copies are waited for at the end of slot 2t+2, before the barrier that
+  // precedes their first reader.
   for (int t = 0; t < T; ++t) {
     const int S = t & 1;
-    ring_stress(t, 2);
-    if (t + 1 < T) {
-      ring_k(min(t + 2, Tm1), S);
-      ring_v(t + 1, S ^ 1);
+    // slot 2t: A softmax of step t; B values of step t-1 and scores of step t
+    if (!grp_b) {
+      softmax(t);
+    } else {
+      if (t > 0) value_mfma(o, pb, lds_v(S ^ 1), voff0, voff1);
+      scores(lds_k(S), s);
+      ken = kebase[t];
     }
-    float alpha;
-    const float c = ldexpf(cq, ken);
-    const v8i pb = (t + 1) * KSTEP <= N ? softmax_step<true>(s, c, m, l, alpha, t * KSTEP, N, g)
-                                        : softmax_step<false>(s, c, m, l, alpha, t * KSTEP, N, g);
-    rescale_o(o, alpha);
-    value_mfma(o, pb, lds_v(S), voff0, voff1);
-    if (t + 1 < T) {
-      scores(lds_k(S ^ 1), s);
-      ken = kebase[t + 1];
+    ring_stress(t, 2);
+    __builtin_amdgcn_s_waitcnt(0x0070);   // the copies of slot 2t-1 landed, LDS reads done
+    asm volatile("s_barrier" ::: "memory");
+    // slot 2t+1: A values of step t and scores of step t+1; B softmax of step t
+    if (t + 2 <= Tm1) ring_k(t + 2, S);
+    if (t + 1 <= Tm1) ring_v(t + 1, S ^ 1);
+    if (!grp_b) {
+      value_mfma(o, pb, lds_v(S), voff0, voff1);
+      if (t + 1 < T) {
+        scores(lds_k(S ^ 1), s);
+        ken = kebase[t + 1];
+      }
+    } else {
+      softmax(t);
     }
     ring_stress(t, 3);
-    __builtin_amdgcn_s_waitcnt(0x0070);   // this step's copies landed, LDS reads done
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): LDS reads done (the copies keep flying)
     asm volatile("s_barrier" ::: "memory");
   }
+  // slot 2T: B values of step T-1
+  if (grp_b) value_mfma(o, pb, lds_v(Tm1 & 1), voff0, voff1);
 
   const int q = q0 + r;
   store_out(o, l, out, vs + (size_t)bh * D, (size_t)bh * N + q, q < N, g);
@@ -1086,11 +1109,11 @@ void launch_attention(const LaunchArgs& a, hipStream_t s) {
                                     (const uint8_t*)a.k_scales, a.v_codes, a.v_scales, (uint16_t*)a.o, a.seq_len,
                                     a.n_pad, tl, tiles, slots);
   } else if (a.fp4) {
-    const int ktiles = a.n_pad / KSTEP;
+    const int ktiles = a.n_pad / KSTEP, tiles4 = (a.n_pad + FP4_WAVES * QW - 1) / (FP4_WAVES * QW);
     auto kern = a.fuse_q ? attn_fp4_kernel<true> : attn_fp4_kernel<false>;
-    kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_expanded,
-                                    (const int*)(a.k_expanded + (size_t)BH * ktiles * KXTILE), a.v_codes,
-                                    a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles, slots);
+    kern<<<BH * tiles4, FP4_T, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_expanded,
+                                       (const int*)(a.k_expanded + (size_t)BH * ktiles * KXTILE), a.v_codes,
+                                       a.v_scales, (uint16_t*)a.o, a.seq_len, a.n_pad, tl, tiles4);
   } else {
     auto kern = a.fuse_q ? attn_fp8_kernel<true> : attn_fp8_kernel<false>;
     kern<<<BH * tiles, 256, 0, s>>>(a.q_codes, a.q_scales, (const uint16_t*)a.q, a.k_codes, a.k_scales,
