@@ -168,13 +168,17 @@ int qsdpa_workspace_layout(const qsdpa_params* p, qsdpa_layout* out);
  * Steps 1-4: channel statistics, K smoothing and the Q/K/V codes and scales,
  * written into the workspace (layout above).  q, k, v: bf16 [B,H,N,128].
  * In FP4 mode it also writes k_expanded from the K codes and scales.
+ * (The quantization of the SDPA inputs, FP8 or FP4 for the query/key side:
+ * hyper.ai/de, the paragraph on GEMM and SDPA quantization and the
+ * SageAttention series; hyper.ai/kr, the paragraph on SDPA quantization.)
  */
 int qsdpa_quantize(const qsdpa_params* p, const void* q, const void* k, const void* v,
                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Steps 5-7 on a workspace filled by qsdpa_quantize with the same params:
- * writes O bf16 [B,H,N,128].
+ * writes O bf16 [B,H,N,128].  (The attention itself kept in FP8: hyper.ai/de,
+ * the paragraph on Table 1; hyper.ai/kr, the paragraph on FP4 against FP8.)
  */
 int qsdpa_attention(const qsdpa_params* p, const void* workspace, size_t ws_bytes, void* o,
                     void* stream);
@@ -194,7 +198,8 @@ int qsdpa_attention_bf16q(const qsdpa_params* p, const void* q, const void* work
 
 /*
  * qsdpa_quantize followed by qsdpa_attention on the same stream: O is
- * bit-identical to the two calls.  The attention kernel quantizes Q itself
+ * bit-identical to the two calls.  (The quantized SDPA in place of the
+ * transformer's BF16 SDPA: hyper.ai/de and hyper.ai/kr, as above.)  The attention kernel quantizes Q itself
  * (as qsdpa_attention_bf16q), so the q_codes and q_scales sections of the
  * workspace are not written by this call.
  */
