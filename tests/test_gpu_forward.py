@@ -431,3 +431,17 @@ def test_forward_on_another_stream_without_workspace(gpu_lib):
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(out), ref)
         del junk
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+def test_forward_many_heads(gpu_lib, fmt):
+    """384 (b,h) pairs of 300 tokens (a query-tile count that is odd in
+    128-token tiles): the per-head offsets of every kernel at a grid far wider
+    than the chip, checked in full on heads at both ends and in between."""
+    B, H, N = 4, 96, 300
+    qb, kb, vb = draw(WORKLOADS["tiny"], batch=B, heads=H, seq_len=N, seed=4096)
+    params = qs.make_params(B, H, N, fmt=fmt, block_q=128)
+    print(f"[forward] many heads B={B} H={H} N={N} fmt={fmt}", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    compare(out, qb, kb, vb, fmt, 128, [(0, 0), (1, 57), (2, 33), (3, 95)], lambda b, h: np.arange(N),
+            f"many-heads {fmt}")

@@ -77,6 +77,15 @@ def test_vc_kontext(gpu_lib):
     check(qb, kb, vb, 128, qs.VC_RHO, [(0, 0), (0, 11), (0, 23)], "kontext1024")
 
 
+def test_vc_gen2048(gpu_lib):
+    """The 2048x2048 shape (B = 2, the classifier-free-guidance pair): 85
+    corrected rows per head (three row groups of 32, so one recomputation
+    workgroup has a wave without rows) over 16896 keys in 15 ranges."""
+    w = WORKLOADS["gen2048_fp8"]
+    qb, kb, vb = draw(w)
+    check(qb, kb, vb, 128, qs.VC_RHO, [(0, 0), (1, 23)], "gen2048_fp8")
+
+
 @pytest.mark.parametrize("N,bq,rho", [(1, 64, 0.005), (65, 64, 0.005), (129, 128, 0.1), (320, 64, 0.005),
                                       (1000, 128, 0.05), (300, 128, 1.0), (2100, 128, 0.02), (17000, 128, 0.005)])
 def test_vc_ragged_and_rho(gpu_lib, N, bq, rho):
