@@ -333,6 +333,7 @@ def main():
                      "algorithmic_GB_s": round(elem * quant_bpe / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_peak_GB_s": HBM_PEAK_GBS},
         "wall_s_timed": round(wall, 3),
+        "system": system_info(dev),
         "per_step_ms": per_step,
     }
     if w.fmt == "fp8":
@@ -372,6 +373,16 @@ def main():
         pool.close()
         pool.join()
     print(json.dumps(rec), flush=True)
+
+
+def system_info(dev) -> dict:
+    """Device, architecture, compute units and HIP / PyTorch versions."""
+    import torch
+
+    pr = torch.cuda.get_device_properties(dev)
+    return {"device": torch.cuda.get_device_name(dev), "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count, "hbm_GiB": round(pr.total_memory / 2 ** 30, 1),
+            "hip": torch.version.hip, "torch": torch.__version__}
 
 
 def kernel_sha() -> str:
