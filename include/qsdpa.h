@@ -67,6 +67,14 @@ extern "C" {
 #define QSDPA_ERR_HIP (-6)                 /* a kernel launch failed */
 #define QSDPA_ERR_SCRATCH_TOO_SMALL (-7)   /* qsdpa_forward_noalloc: workspace > QSDPA_SCRATCH_BYTES */
 
+/* Size limits, checked before any launch.  N above QSDPA_MAX_SEQ_LEN or
+ * B*H above QSDPA_MAX_BH give QSDPA_ERR_UNSUPPORTED; B*H*round_up(N, 128)*128
+ * above QSDPA_MAX_ELEMS (elements of one padded tensor) gives
+ * QSDPA_ERR_INVALID_ARG. */
+#define QSDPA_MAX_SEQ_LEN (1 << 22)
+#define QSDPA_MAX_BH 65535
+#define QSDPA_MAX_ELEMS (1LL << 36)
+
 /* Size of the static scratch array of qsdpa_forward_noalloc (96 MiB per GPU):
  * enough for the Kontext workload [1, 24, 8704, 128] in FP8 and MXFP4 mode. */
 #define QSDPA_SCRATCH_BYTES (96u << 20)
@@ -83,9 +91,9 @@ extern "C" {
 #define QSDPA_QK_MXFP4_E2M1 2
 
 typedef struct qsdpa_params {
-  int32_t batch;         /* B >= 1 */
+  int32_t batch;         /* B >= 1, B*H <= QSDPA_MAX_BH */
   int32_t heads;         /* H >= 1 */
-  int32_t seq_len;       /* N >= 1 (any value: tails are handled) */
+  int32_t seq_len;       /* 1 <= N <= QSDPA_MAX_SEQ_LEN (any value: tails are handled) */
   int32_t head_dim;      /* must be 128 */
   int32_t block_q;       /* FP8 mode: Q tokens per scale, 64 or 128 (ignored in the FP4 modes) */
   int32_t block_k;       /* FP8 mode: K tokens per scale, must be 64 (ignored in the FP4 modes) */

@@ -24,6 +24,9 @@ QSDPA_ERR_ALIAS = -5
 QSDPA_ERR_HIP = -6
 QSDPA_ERR_SCRATCH_TOO_SMALL = -7
 QSDPA_SCRATCH_BYTES = 96 << 20   # the static scratch array of qsdpa_forward_noalloc, per GPU
+MAX_SEQ_LEN = 1 << 22             # QSDPA_MAX_SEQ_LEN: longest sequence accepted
+MAX_BH = 65535                    # QSDPA_MAX_BH: largest B*H accepted
+MAX_ELEMS = 1 << 36               # QSDPA_MAX_ELEMS: largest B*H*round_up(N, 128)*128
 QSDPA_QK_FP8_E4M3 = 0
 QSDPA_QK_FP4_E2M1 = 1
 QSDPA_QK_MXFP4_E2M1 = 2

@@ -15,8 +15,6 @@
 namespace {
 
 constexpr uint64_t kAlign = 256;
-constexpr int64_t kMaxElems = (int64_t)1 << 36;  // B*H*N*128 bf16 elements per tensor
-constexpr int kMaxSeq = 1 << 22;
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -24,11 +22,11 @@ int check_params(const qsdpa_params* p) {
   if (!p) return QSDPA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->heads < 1 || p->seq_len < 1) return QSDPA_ERR_INVALID_ARG;
   if (p->head_dim != QSDPA_HEAD_DIM) return QSDPA_ERR_UNSUPPORTED;
-  if (p->seq_len > kMaxSeq) return QSDPA_ERR_UNSUPPORTED;
+  if (p->seq_len > QSDPA_MAX_SEQ_LEN) return QSDPA_ERR_UNSUPPORTED;
   const int64_t bh = (int64_t)p->batch * p->heads;
-  if (bh > 65535) return QSDPA_ERR_UNSUPPORTED;  // grid y / flattened grid limits
+  if (bh > QSDPA_MAX_BH) return QSDPA_ERR_UNSUPPORTED;  // grid y / flattened grid limits
   const int64_t n_pad = ((int64_t)p->seq_len + 127) / 128 * 128;
-  if (bh * n_pad * QSDPA_HEAD_DIM > kMaxElems) return QSDPA_ERR_INVALID_ARG;
+  if (bh * n_pad * QSDPA_HEAD_DIM > QSDPA_MAX_ELEMS) return QSDPA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale)) return QSDPA_ERR_INVALID_ARG;
   if (p->qk_format == QSDPA_QK_FP8_E4M3) {
     if (p->block_q != 64 && p->block_q != 128) return QSDPA_ERR_UNSUPPORTED;

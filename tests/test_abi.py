@@ -57,6 +57,28 @@ def test_invalid_params(change, status):
     assert lib.qsdpa_forward(ctypes.byref(p), 256, 256, 256, 1 << 40, 1 << 41, 1 << 30, None) == status
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+def test_size_limits_are_exact(fmt):
+    """The largest accepted N and B*H pass, one more is refused."""
+    ok = qs.make_params(1, 1, qs.MAX_SEQ_LEN, fmt=fmt)
+    assert qs.qsdpa_validate_params(ok) == qs.QSDPA_OK
+    assert qs.qsdpa_workspace_bytes(ok) > 0
+    assert qs.qsdpa_validate_params(qs.make_params(1, 1, qs.MAX_SEQ_LEN + 1, fmt=fmt)) == qs.QSDPA_ERR_UNSUPPORTED
+    assert qs.qsdpa_validate_params(qs.make_params(5, qs.MAX_BH // 5, 64, fmt=fmt)) == qs.QSDPA_OK
+    assert qs.qsdpa_validate_params(qs.make_params(2, (qs.MAX_BH + 1) // 2, 64, fmt=fmt)) == qs.QSDPA_ERR_UNSUPPORTED
+    # B*H*n_pad*128 at the element limit, then one 128-token tile more
+    assert qs.qsdpa_validate_params(qs.make_params(4096, 1, 1 << 17, fmt=fmt)) == qs.QSDPA_OK
+    assert qs.qsdpa_validate_params(qs.make_params(4096, 1, (1 << 17) + 1, fmt=fmt)) == qs.QSDPA_ERR_INVALID_ARG
+
+
+def test_header_limits_match_binding():
+    import os
+    hdr = open(os.path.join(os.path.dirname(qs.PKG), "include", "qsdpa.h")).read()
+    assert "#define QSDPA_MAX_SEQ_LEN (1 << 22)" in hdr and qs.MAX_SEQ_LEN == 1 << 22
+    assert "#define QSDPA_MAX_BH 65535" in hdr and qs.MAX_BH == 65535
+    assert "#define QSDPA_MAX_ELEMS (1LL << 36)" in hdr and qs.MAX_ELEMS == 1 << 36
+
+
 def test_fp4_group_checked_only_in_fp4_mode():
     p = qs.make_params(1, 1, 64, fmt="fp4", fp4_group=32)
     assert qs.qsdpa_validate_params(p) == qs.QSDPA_ERR_UNSUPPORTED

@@ -105,6 +105,59 @@ def test_forward_long_sequence(gpu_lib, fmt):
     compare(out, qb, kb, vb, fmt, 128, [(0, 0)], lambda b, h: rows, f"long-{fmt}")
 
 
+def _max_length_inputs():
+    """Q = 0 and K, V [1, 1, 2^22, 128] whose values are E4M3 values times
+    2^-8 (random codes, the NaN patterns excluded), with +1.75 = 448 * 2^-8 at
+    one token of every V channel.  So vmax = 1.75, the V scale is exactly
+    2^-8 and every V value is its own dequantized code (checked against the
+    oracle on a slice): O is the mean of V itself, which fp64 sums exactly.
+    Drawn as bytes through a 256-entry table, 2^29 values take seconds."""
+    N = qs.MAX_SEQ_LEN
+    rng = np.random.default_rng(4242)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F])
+    table = oracle.f64_to_bf16_bits(oracle.decode(finite, oracle.E4M3) * 2.0 ** -8)
+
+    def bits():
+        return table[rng.integers(0, table.size, (1, 1, N, 128), dtype=np.uint8)]
+
+    kb, vb = bits(), bits()
+    vb[0, 0, rng.integers(0, N, 128), np.arange(128)] = oracle.f64_to_bf16_bits(np.array(1.75))
+    # the premise, on the first 2^16 tokens: the oracle's codes times its scale give V back
+    v0 = oracle.bf16_bits_to_f64(vb[:, :, :1 << 16])
+    codes, scale = oracle.quantize_v(v0, np.full((1, 1, 128), 1.75, np.float32))
+    assert np.all(scale == np.float32(2.0 ** -8))
+    assert np.array_equal(oracle.decode(codes, oracle.E4M3) * 2.0 ** -8, v0)
+    mean_v = np.zeros(128)
+    for t0 in range(0, N, 1 << 18):
+        mean_v += oracle.bf16_bits_to_f64(vb[0, 0, t0:t0 + (1 << 18)]).sum(axis=0)
+    mean_v /= N
+    return np.zeros_like(kb), kb, vb, oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(mean_v))
+
+
+_MAX_LENGTH = {}
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+def test_forward_maximum_length_zero_queries(gpu_lib, fmt):
+    """One head at the largest sequence length the library accepts (2^22
+    tokens: 65536 online-softmax steps, 32768 query tiles, 16384 statistics
+    ranges).  With Q = 0 every P code is 448 and O is the mean of the
+    dequantized V codes for every query row; the inputs make that the mean
+    of V itself."""
+    if not _MAX_LENGTH:
+        _MAX_LENGTH["inputs"] = _max_length_inputs()
+    qb, kb, vb, want = _MAX_LENGTH["inputs"]
+    N = qb.shape[2]
+    params = qs.make_params(1, 1, N, fmt=fmt)
+    print(f"[forward] maximum length N={N} fmt={fmt}, Q = 0", flush=True)
+    out = run_forward(qb, kb, vb, params)
+    got = oracle.bf16_bits_to_f64(out[0, 0])
+    err = np.max(np.abs(got - want[None, :]))
+    print(f"[forward] maximum length {fmt}: max |O - mean V| {err:.3e} (|mean V| up to {np.abs(want).max():.3e})",
+          flush=True)
+    assert err <= 2.0 ** -8 * np.abs(want).max()
+
+
 # Ragged cases whose raw max-abs exceeds 1e-2, and why.  N = 129, FP8,
 # block_q = 64, batch 1, query 65, channel 96: the weight of key 3 in the first
 # step is 448 p = 304.000731, 2.4e-6 above the E4M3 midpoint 304 between codes
