@@ -39,7 +39,9 @@
  *   - Device pointers must be 16-byte aligned, the workspace 256-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; the library never allocates, frees or
- *     synchronizes, and keeps no state between calls (thread-safe).
+ *     synchronizes, and keeps no state between calls (thread-safe).  The one
+ *     exception is qsdpa_forward_noalloc: its static scratch array is shared by
+ *     every call on a GPU (see there).
  *   - Every argument is validated before the first launch: a negative status
  *     means nothing was enqueued (except QSDPA_ERR_HIP, which reports a failed
  *     launch).  Nothing throws across the ABI.  Inputs must be finite.
