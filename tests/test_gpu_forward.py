@@ -240,12 +240,13 @@ def test_constant_values_stay_constant(gpu_lib):
     assert rel.max() <= 2.0 ** -4 + N * 2.0 ** -10 / 448 + 2.0 ** -8
 
 
-def test_deterministic_and_in_bounds(gpu_lib):
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+def test_deterministic_and_in_bounds(gpu_lib, fmt):
     """Bitwise-identical repeats; nothing written outside O or the workspace."""
     w = WORKLOADS["tiny"]
     N = 1000
     qb, kb, vb = draw(w, batch=1, heads=3, seq_len=N, seed=21)
-    params = qs.make_params(1, 3, N)
+    params = qs.make_params(1, 3, N, fmt=fmt)
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
     numel = 3 * N * 128
     guard = 4096
