@@ -142,6 +142,38 @@ def test_quantize_e2m1_ties(gpu_lib, fmt):
     check_quantize(qb, kb, vb, fmt, 128, [(0, 0)], f"ties-{fmt}")
 
 
+@pytest.mark.parametrize("bq", [64, 128])
+def test_quantize_e4m3_every_bf16_value(gpu_lib, bq):
+    """The device E4M3 encoder against the oracle's on every finite bf16 value
+    of magnitude up to 448 (34754 values: zeros, subnormals, every E4M3 code,
+    tie and midpoint neighbour a bf16 value can be), at unit scale: every Q
+    and K scale block and every V channel also holds 448, so each inverse scale
+    is 448 / 448 = 1 and each code is E4M3 of the input itself.  K's second
+    half is its first half negated, so its channel means are exactly 0 and the
+    smoothing leaves it unchanged."""
+    top = 0x43E0                                  # bf16 bits of 448
+    pos = np.arange(top + 1, dtype=np.uint16)      # +0 .. 448
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+    N = 320
+
+    def filled(src, n_tok, rows, cols):
+        """n_tok x 128 bf16 patterns: 448 at (rows, cols), src (repeated) elsewhere"""
+        x = np.zeros((n_tok, 128), np.uint16)
+        mark = np.zeros((n_tok, 128), bool)
+        mark[rows, cols] = True
+        x[mark] = top
+        x[~mark] = np.resize(src, int((~mark).sum()))
+        return x
+
+    q = filled(vals, N, np.arange(0, N, 64), 0)                # a 448 in every 64-token block
+    v = filled(vals[::-1], N, 0, np.arange(128))               # a 448 in every channel
+    kh = filled(pos, N // 2, [0, 64, 128], 1)                  # with the negated half: 448 in every block
+    k = np.concatenate([kh, kh ^ np.uint16(0x8000)])
+    shaped = lambda x: x.reshape(1, 1, N, 128)
+    assert np.isin(vals, q).all() and np.isin(vals, k).all() and np.isin(vals, v).all()
+    check_quantize(shaped(q), shaped(k), shaped(v), "fp8", bq, [(0, 0)], f"every-bf16-bq{bq}")
+
+
 @pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp4", 128), ("mxfp4", 128)])
 def test_quantize_k_mean_exact_beyond_fp64_range(gpu_lib, fmt, bq):
     """K channels whose values span more binades than fp64 partial sums hold
