@@ -174,6 +174,37 @@ def test_quantize_e4m3_every_bf16_value(gpu_lib, bq):
     check_quantize(shaped(q), shaped(k), shaped(v), "fp8", bq, [(0, 0)], f"every-bf16-bq{bq}")
 
 
+@pytest.mark.parametrize("fmt", ["fp4", "mxfp4"])
+def test_quantize_e2m1_every_bf16_value(gpu_lib, fmt):
+    """The device E2M1 encoder against the oracle's on every finite bf16 value
+    of magnitude up to 6 (33154 values), at unit scale: every 16-channel group
+    of every Q and K token holds a 6, so the FP4 scale is 6 / 6 = 1 and the
+    MXFP4 shared exponent is floor(log2 6) - 2 = 0, and each code is E2M1 of
+    the input itself.  K's second half is its first half negated (channel
+    means exactly 0); V holds the same values."""
+    top = 0x40C0                                  # bf16 bits of 6
+    pos = np.arange(top + 1, dtype=np.uint16)      # +0 .. 6
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+    N = 320
+
+    def filled(src, n_tok):
+        """n_tok x 128 bf16 patterns: 6 at channel 16 j of every token, src (repeated) elsewhere"""
+        x = np.zeros((n_tok, 128), np.uint16)
+        mark = np.zeros((n_tok, 128), bool)
+        mark[:, ::16] = True
+        x[mark] = top
+        x[~mark] = np.resize(src, int((~mark).sum()))
+        return x
+
+    q = filled(vals, N)
+    v = filled(vals[::-1], N)
+    kh = filled(pos, N // 2)
+    k = np.concatenate([kh, kh ^ np.uint16(0x8000)])
+    shaped = lambda x: x.reshape(1, 1, N, 128)
+    assert np.isin(vals, q).all() and np.isin(vals, k).all()
+    check_quantize(shaped(q), shaped(k), shaped(v), fmt, 128, [(0, 0)], f"every-bf16-{fmt}")
+
+
 @pytest.mark.parametrize("fmt,bq", [("fp8", 64), ("fp4", 128), ("mxfp4", 128)])
 def test_quantize_k_mean_exact_beyond_fp64_range(gpu_lib, fmt, bq):
     """K channels whose values span more binades than fp64 partial sums hold
