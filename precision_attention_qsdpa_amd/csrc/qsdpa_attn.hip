@@ -4,12 +4,14 @@
 // the scaled MFMA in its FP4 format, same ring and schedule) and
 // attn_fp4_kernel (FP4 Q/K codes with fp32 scales per 16 channels, scores
 // from f16 hi parts plus FP8 hi/lo corrections).  What follows describes the
-// structure all share.
+// structure all share; the FP4 kernel's workgroups differ (8 waves in two
+// groups, one workgroup per CU, described at that kernel).
 //
-// Work split: one workgroup = 4 waves = 128 consecutive queries of one (b,h);
-// each wave owns 32 queries and walks all keys in steps of 64, in ascending
-// order (the online-softmax step of the method).  Two workgroups share a CU,
-// so each SIMD runs two waves whose MFMA and softmax phases interleave.
+// Work split: each wave owns 32 consecutive queries of one (b,h) and walks
+// all keys in steps of 64, in ascending order (the online-softmax step of the
+// method).  In the FP8 and MXFP4 kernels a workgroup is 4 waves = 128 queries
+// and two workgroups share a CU, so each SIMD runs two waves whose MFMA and
+// softmax phases interleave.
 //
 // Per 64-key step t a wave computes
 //   S^T (64 keys x 32 queries) = K_tile . Q^T      (MFMA, keys on rows)
@@ -281,8 +283,8 @@ __device__ __forceinline__ void ring_stress(int, int) {}
 #endif
 
 // The ring's start: K(0), K(1), K(2), V(0), K(3), V(1), in that order, so
-// that from the first step on the copies go out as K(t+3), V(t) pairs: K(0)
-// K(1) K(2) V(0) | K(3) V(1) | K(4) V(2) | ...  (K(t+4) and V(t+2) issued
+// that after K(0) and K(1) the copies go out as K(j+2), V(j) pairs: K(0)
+// K(1) | K(2) V(0) | K(3) V(1) | K(4) V(2) | ...  (K(t+4) and V(t+2) issued
 // by step t).  A wave then has 2t + 8 copy groups (2 copies each) issued by
 // the end of step t, and a wait for at most 8 outstanding copies means the
 // first 2t + 4 groups landed, the last two of them K(t+2) and V(t): the
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
 
   // steps 0 .. T-2 (full)
   // Instruction order of a step: the 8 MFMAs (4 scores, 4 values) spread
-  // over the ~170 VALU instructions of the softmax, 22 after each, and the
+  // over the ~150 VALU instructions of the softmax, 19 after each, and the
   // two LDS reads of each MFMA operand issued right after the MFMA before it.
   auto step = [&](int t, v16f* s_cur, v16f* s_next, auto st) {
     constexpr int S = decltype(st)::value;   // t % 4
