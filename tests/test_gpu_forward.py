@@ -227,14 +227,15 @@ def test_forward_tiny_magnitudes(gpu_lib, fmt, bq):
     compare(out, qb, kb, vb, fmt, bq, [(0, 0), (0, 1)], lambda b, h: np.arange(N), f"tiny-{fmt}-bq{bq}")
 
 
-def test_constant_values_stay_constant(gpu_lib):
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+def test_constant_values_stay_constant(gpu_lib, fmt):
     """V = c per channel: O/c = sum(P)/(448 l) within the E4M3 weight bound."""
     N = 2000
     qb, kb, _ = draw(WORKLOADS["tiny"], heads=1, seq_len=N, seed=11)
     c = np.linspace(0.5, 3.0, 128).astype(np.float32)
     from workloads import to_bf16_bits
     vb = to_bf16_bits(np.broadcast_to(c, (1, 1, N, 128)).copy())
-    out = run_forward(qb, kb, vb, qs.make_params(1, 1, N))
+    out = run_forward(qb, kb, vb, qs.make_params(1, 1, N, fmt=fmt))
     cv = oracle.bf16_bits_to_f64(vb)[0, 0, 0]
     rel = np.abs(oracle.bf16_bits_to_f64(out[0, 0]) / cv - 1)
     assert rel.max() <= 2.0 ** -4 + N * 2.0 ** -10 / 448 + 2.0 ** -8
@@ -438,18 +439,18 @@ def test_offsets_beyond_4gib(gpu_lib, fmt):
 
 
 def test_concurrent_streams_match_serial(gpu_lib):
-    """Two forwards on two streams at once (own inputs, outputs and
-    workspaces) give the serial results bit for bit: the library keeps no
-    state between calls."""
-    shapes = [("fp8", 1500, 3), ("mxfp4", 2100, 2)]
+    """Forwards in the three modes on three streams at once (own inputs,
+    outputs and workspaces) give the serial results bit for bit: the library
+    keeps no state between calls."""
+    shapes = [("fp8", 1500, 3), ("mxfp4", 2100, 2), ("fp4", 900, 2)]
     inputs, serial = [], []
     for fmt, N, H in shapes:
         qb, kb, vb = draw(WORKLOADS["tiny"], heads=H, seq_len=N, seed=N)
         params = qs.make_params(1, H, N, fmt=fmt, block_q=128)
         inputs.append((to_dev(qb), to_dev(kb), to_dev(vb), params))
         serial.append(run_forward(qb, kb, vb, params))
-    print("[forward] two streams", flush=True)
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    print("[forward] three streams", flush=True)
+    streams = [torch.cuda.Stream() for _ in shapes]
     outs = []
     torch.cuda.synchronize()
     for rep in range(3):
@@ -461,7 +462,7 @@ def test_concurrent_streams_match_serial(gpu_lib):
                 outs.append((o, ws))
     torch.cuda.synchronize()
     for i, (o, _) in enumerate(outs):
-        assert np.array_equal(from_dev(o), serial[i % 2]), f"stream result {i} differs"
+        assert np.array_equal(from_dev(o), serial[i % len(shapes)]), f"stream result {i} differs"
 
 
 def test_forward_on_another_stream_without_workspace(gpu_lib):
