@@ -438,6 +438,31 @@ def test_offsets_beyond_4gib(gpu_lib, fmt):
             f"4GiB-{fmt}")
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "mxfp4"])
+def test_forward_maximum_heads(gpu_lib, fmt):
+    """B*H = 65535, the largest number of (b,h) pairs the library accepts
+    (the statistics and quantize grids' second dimension), 100 tokens each
+    (a ragged single tile).  Five heads spread over the batch, the first and
+    the last among them, are checked against the oracle on every row."""
+    B, H, N = 5, 13107, 100
+    assert B * H == qs.MAX_BH
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(65535)
+    shape = (B, H, N, 128)
+    q = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    params = qs.make_params(B, H, N, fmt=fmt, block_q=128)
+    print(f"[forward] maximum heads fmt={fmt} B={B} H={H} N={N}", flush=True)
+    out = qs.qsdpa_forward(q, k, v, params=params)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (1, 4242), (2, H // 2), (3, 77), (B - 1, H - 1)]
+    pick = lambda t: np.stack([from_dev(t[b, h]) for b, h in heads])[None]
+    qb, kb, vb, ob = pick(q), pick(k), pick(v), pick(out)
+    compare(ob, qb, kb, vb, fmt, 128, [(0, i) for i in range(len(heads))], lambda b, h: np.arange(N),
+            f"max-heads-{fmt}")
+
+
 def test_concurrent_streams_match_serial(gpu_lib):
     """Forwards in the three modes on three streams at once (own inputs,
     outputs and workspaces) give the serial results bit for bit: the library

@@ -106,3 +106,16 @@ def test_vc_ties_go_to_the_lower_index(gpu_lib):
         assert np.all(err[0, h] == err[0, h, 0])
         assert np.array_equal(sel[0, h], np.arange(10))
     check(qb, kb, vb, 128, 0.01, [(0, 0), (0, 1)], "ties")
+
+
+def test_vc_maximum_heads(gpu_lib):
+    """B*H = 65535 (the largest accepted), 100 tokens each: one corrected row
+    per head, 65535 selection workgroups and a recomputation grid of 65535
+    workgroups; three heads spread over the batch are checked."""
+    B, H, N = 5, 13107, 100
+    assert B * H == qs.MAX_BH
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(65536)
+    bits = [from_dev(torch.randn((B, H, N, 128), generator=gen, device="cuda", dtype=torch.bfloat16))
+            for _ in range(3)]
+    check(*bits, 128, qs.VC_RHO, [(0, 0), (2, H // 2), (B - 1, H - 1)], "max-heads")
